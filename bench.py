@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-adapter LoRA linear on one MI355X (gfx950).
+
+Workload: one Llama-3-8B decode step of q_proj. T = 64 tokens, 4096 -> 4096,
+a 9-slot pool per layer (slots 1-8 rank 16, alpha 32; slot 0 the zero
+adapter), 8 adapters x 8 tokens in shuffled order, over 32 layers, each with
+its own seeded weights and pool (so a step streams ~1.1 GB, far beyond the
+256 MB MALL). One step = the host plan (lora_plan) and its upload, then the
+32 lora_linear calls, replayed from a HIP graph captured once.
+
+value = T * layers / step time: tokens through one adapted linear per second
+(T / mean lora_linear time).
+
+After the timed region the same step runs eagerly with the library's
+per-kernel HIP-event timing on (behind a long filler GEMM so the host stays
+ahead of the GPU); those durations give the roofline figures. Then the
+prefill-shaped gate projection (T = 8192, 4096 -> 14336) is timed the same
+way for the base GEMM's matrix-core fraction, and the fp64 CPU oracle is
+timed on a bounded sample of the decode workload.
+
+Prints one JSON line. --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mixed-LoRA linear tokens/s + % MFMA/HBM roofline at Llama-3-8B shapes"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager calls instead of a graph replay")
+    return ap.parse_args()
+
+
+def stage_bytes(ids, ranks, d_in, d_out, r_max, es=2):
+    """Algorithmic bytes per launch of each stage."""
+    from rank_gemm_amd import accounting as acc
+    seg = acc.segments(ids, ranks)
+    T_a = sum(seg.values())
+    shrink = es * T_a * d_in + sum(es * int(ranks[s]) * d_in for s in seg) + 4 * T_a * r_max
+    expand = sum(es * int(ranks[s]) * d_out for s in seg) + 4 * T_a * r_max + 2 * es * T_a * d_out
+    assert shrink + expand == acc.correction_bytes(ids, ranks, d_in, d_out, es, r_max)
+    return {"base": acc.base_bytes(len(ids), d_in, d_out, es), "shrink": shrink, "expand": expand}
+
+
+def group_stages(stats):
+    """Kernel stats -> per-call stage durations (us)."""
+    def us(name):
+        return stats[name]["mean_ms"] * 1e3 if name in stats else 0.0
+    return {
+        "base": us("gemm_bf16") + us("gemm_splitk_reduce"),
+        "shrink": us("sgmv_shrink"),
+        "expand": us("sgmv_expand"),
+    }
+
+
+def filler(torch, ms_target=60.0):
+    """Queue ~ms_target of GPU work so the host can run ahead of the GPU."""
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    n = max(1, int(ms_target / 1.0))
+    for _ in range(n):
+        a = torch.matmul(a, a) * 1e-2
+    return a
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rank_gemm_amd import accounting as acc
+    from rank_gemm_amd import lora
+    from rank_gemm_amd.inputs import make_config
+
+    lora.lib()  # fail loudly if the library was not built
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    torch.cuda.set_device(0)
+    L = args.layers
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(8) as ex:
+        ws_host = list(ex.map(lambda l: make_config(2, layer=l), range(L)))
+    log(f"generated {L} layers in {time.perf_counter() - t0:.1f}s")
+    w0 = ws_host[0]
+    T, S, r_max = w0.T, w0.S, w0.r_max
+    ids = w0.slot_ids
+    d_in, d_out = w0.projections[0].d_in, w0.projections[0].d_out
+    ranks = w0.ranks
+
+    pools, xs, Ws, ys = [], [], [], []
+    for w in ws_host:
+        pr = w.projections[0]
+        pool = lora.Pool(S, r_max, d_in, d_out, "bf16")
+        for s, a in sorted(pr.adapters.items()):
+            pool.install(s, lora.to_device(a.A, "bf16"), lora.to_device(a.B, "bf16"), a.alpha)
+        pools.append(pool)
+        xs.append(lora.to_device(pr.x, "bf16"))
+        Ws.append(lora.to_device(pr.W, "bf16"))
+        ys.append(torch.empty((T, d_out), dtype=torch.bfloat16, device="cuda"))
+    ws = torch.empty(pools[0].workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    p = lora.plan(ids, S)
+    info0 = (p.info.T, p.info.S, p.info.T_a, p.info.k, p.info.n_items, p.info.max_seg)
+    torch.cuda.synchronize()
+
+    def layers_once():
+        for l in range(L):
+            lora.linear(xs[l], Ws[l], pools[l], p, y=ys[l], workspace=ws)
+
+    def step_plan():
+        lora.plan_into(p, ids)
+        assert (p.info.T, p.info.S, p.info.T_a, p.info.k, p.info.n_items, p.info.max_seg) == info0
+
+    # ---- timed region: graph replay (default) or eager --------------------------
+    graph = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                layers_once()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layers_once()
+        torch.cuda.synchronize()
+
+    def step():
+        step_plan()
+        if graph is not None:
+            graph.replay()
+        else:
+            layers_once()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = T * L * args.steps / elapsed
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.4g} tokens/s")
+
+    # ---- per-kernel durations (HIP events on the launch stream) -------------------
+    f = filler(torch)
+    lora.profile_begin(8 * L * args.profile_steps + 64)
+    for _ in range(args.profile_steps):
+        step_plan()
+        layers_once()
+    stats = lora.profile_end()
+    torch.cuda.synchronize()
+    del f
+    st = group_stages(stats)
+    sb = stage_bytes(ids, ranks, d_in, d_out, r_max)
+    stage_gbs = {k: (sb[k] / (st[k] * 1e-6) / 1e9 if st[k] > 0 else None) for k in sb}
+    dominant = max(st, key=lambda k: st[k])
+    base_flops = acc.base_flops(T, d_in, d_out)
+    ai = base_flops / sb["base"]
+    bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    kernel_names = {"base": "gemm_bf16" + ("+gemm_splitk_reduce" if "gemm_splitk_reduce" in stats else ""),
+                    "shrink": "sgmv_shrink", "expand": "sgmv_expand"}
+    if bound == "hbm" or dominant != "base":
+        achieved = stage_gbs[dominant]
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": kernel_names[dominant], "bytes_per_launch": sb[dominant],
+                "mean_us": round(st[dominant], 3)}
+    else:
+        tf = base_flops / (st["base"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": kernel_names["base"],
+                "mean_us": round(st["base"], 3)}
+    se_us = st["shrink"] + st["expand"]
+    se_bytes = sb["shrink"] + sb["expand"]
+    corr = {"bytes_per_call": se_bytes, "shrink_us": round(st["shrink"], 3), "expand_us": round(st["expand"], 3),
+            "achieved_gbs": round(se_bytes / (se_us * 1e-6) / 1e9, 1) if se_us > 0 else None,
+            "frac_hbm": round(se_bytes / (se_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) if se_us > 0 else None}
+    kernels = {k: {"mean_us": round(v["mean_ms"] * 1e3, 3), "min_us": round(v["min_ms"] * 1e3, 3),
+                   "count": v["count"]} for k, v in stats.items()}
+    log(f"kernels: {kernels}")
+
+    # ---- prefill-shaped base GEMM (matrix-core fraction) --------------------------
+    prefill = None
+    if not args.no_prefill:
+        del pools, xs, Ws, ys
+        torch.cuda.empty_cache()
+        w3 = make_config(3)
+        pr = w3.projections[0]
+        pool3 = lora.Pool(w3.S, w3.r_max, pr.d_in, pr.d_out, "bf16")
+        for s, a in sorted(pr.adapters.items()):
+            pool3.install(s, lora.to_device(a.A, "bf16"), lora.to_device(a.B, "bf16"), a.alpha)
+        x3, W3 = lora.to_device(pr.x, "bf16"), lora.to_device(pr.W, "bf16")
+        p3 = lora.plan(w3.slot_ids, w3.S)
+        y3 = torch.empty((w3.T, pr.d_out), dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            lora.linear(x3, W3, pool3, p3, y=y3)
+        torch.cuda.synchronize()
+        n3 = 10
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(n3):
+            lora.linear(x3, W3, pool3, p3, y=y3)
+        ev1.record()
+        torch.cuda.synchronize()
+        call_ms = ev0.elapsed_time(ev1) / n3
+        lora.profile_begin(8 * n3 + 64)
+        for _ in range(n3):
+            lora.linear(x3, W3, pool3, p3, y=y3)
+        s3 = lora.profile_end()
+        st3 = group_stages(s3)
+        fl = acc.base_flops(w3.T, pr.d_in, pr.d_out)
+        tf = fl / (st3["base"] * 1e-6) / 1e12
+        sb3 = stage_bytes(w3.slot_ids, w3.ranks, pr.d_in, pr.d_out, w3.r_max)
+        prefill = {"workload": "llama3-8b gate_proj prefill T=8192 4096->14336, 16 seqs x 512, S=17 rank 16",
+                   "base_gemm_us": round(st3["base"], 2), "base_tflops": round(tf, 1),
+                   "base_frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+                   "shrink_us": round(st3["shrink"], 2), "expand_us": round(st3["expand"], 2),
+                   "correction_frac_hbm": round((sb3["shrink"] + sb3["expand"]) /
+                                                ((st3["shrink"] + st3["expand"]) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                   if st3["shrink"] + st3["expand"] > 0 else None,
+                   "call_ms": round(call_ms, 4), "tokens_per_s": round(w3.T / (call_ms * 1e-3), 1),
+                   "kernels": {k: round(v["mean_ms"] * 1e3, 2) for k, v in s3.items()}}
+        log(f"prefill: {prefill}")
+
+    # ---- CPU oracle baseline (bounded sample of the same workload) ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        done, t0 = 0, time.perf_counter()
+        while done < L and time.perf_counter() - t0 < args.cpu_seconds:
+            pr = ws_host[done].projections[0]
+            oracle.lora_rows("bf16", pr.x, pr.W, S, pr.adapters, ids)
+            done += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(T * done / el, 2), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"fp64 oracle, all {T} rows of {done} q_proj layer(s) of the decode workload, "
+                         f"{el:.1f} s"}
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama3-8b q_proj decode step: T={T}, {d_in}->{d_out}, S={S} (8 adapters x 8 "
+                               f"tokens, rank 16, alpha 32), {L} layers, plan + {L} lora_linear per step",
+                   "T": T, "d_in": d_in, "d_out": d_out, "S": S, "rank": 16, "layers": L,
+                   "mode": "eager" if graph is None else "hip graph replay"},
+        "roofline": roof, "cpu_baseline": cpu,
+        "correction": corr, "kernels": kernels, "prefill": prefill,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * liblora: mixed-adapter LoRA linear layer for AMD Instinct MI355X (gfx950).
+ *
+ *   y_i = x_i W^T + (alpha_s / r_s) (x_i A_s^T) B_s^T,   s = slot_ids[i]
+ *
+ * The base GEMM runs once over every row; each row's slot selects a resident
+ * adapter in a fixed device slot pool, and the low-rank correction is
+ * applied as a segmented gather shrink (x -> [T, r] fp32) and expand
+ * ([T, r] -> y). Row formula: "43. Beyond text: images, embeddings,
+ * reranking and many LoRAs" (inference.shantanugoel.com), section "Many
+ * adapters, one base-model batch". Slot 0 is the zero adapter (rank 0,
+ * scaling 0) that every base-only row addresses and that the kernels skip:
+ * "mstar.engine.resources.lora.pool" (mstar.stanford.edu), module text.
+ *
+ * Conventions for every call:
+ *  - Every function returns LORA_OK (0) or a negative LORA_E* status; no C++
+ *    exception crosses this interface. lora_status_string() names a status.
+ *  - "dev" pointers are HIP device memory, "host" pointers are CPU memory.
+ *    The caller owns every buffer passed in; the library keeps only the
+ *    small host-side pool handle (plus a 4-byte device status word).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Device work is
+ *    asynchronous on it unless a call says it synchronises.
+ *  - Matrices are row-major and contiguous. Element offsets are computed in
+ *    64-bit, so T*d may exceed 2^31 ("Silent: int32 overflow at long
+ *    context", "LoRA serving, embeddings, rerankers, pooling",
+ *    mlinterviewnotes.com).
+ *  - Element type is the pool's: LORA_BF16 (uint16 bf16 bit patterns,
+ *    fp32 accumulation, y rounded to nearest even) or LORA_F32.
+ *  - Widths: d_in must be a multiple of 8; d_out, T and S are otherwise
+ *    free (ragged tails are masked).
+ */
+#ifndef RANK_GEMM_AMD_LORA_H
+#define RANK_GEMM_AMD_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define LORA_OK 0
+#define LORA_EINVAL (-1)     /* null pointer, bad size, plan/pool mismatch */
+#define LORA_ESLOT (-2)      /* slot id out of range */
+#define LORA_ERANK (-3)      /* rank outside [1, r_max] */
+#define LORA_ENONFINITE (-4) /* adapter weights or alpha not finite */
+#define LORA_EHIP (-5)       /* a HIP runtime call or kernel launch failed */
+#define LORA_ESPACE (-6)     /* a caller buffer is too small */
+
+/* element types */
+#define LORA_F32 0
+#define LORA_BF16 1
+
+/* rows per work item of the plan (one 16-row matrix-core tile) */
+#define LORA_PLAN_ROWS 16
+
+typedef struct lora_pool lora_pool;
+
+/* Summary of one plan; filled by lora_plan, read by lora_linear. */
+typedef struct lora_plan_info {
+    int32_t T;       /* tokens in the step */
+    int32_t S;       /* slot count the plan was built for */
+    int32_t T_a;     /* tokens whose slot is not 0 */
+    int32_t k;       /* distinct non-zero slots that have tokens */
+    int32_t n_items; /* entries in the work list */
+    int32_t max_seg; /* longest non-zero segment, in tokens */
+} lora_plan_info;
+
+/*
+ * Create a pool handle over caller-owned device buffers and zero every slot.
+ * Layout ("stacked" slot buffers padded to a common maximum rank, unused rows
+ * of A and columns of B zero: shantanugoel page, "Many adapters, one
+ * base-model batch"; mlinterviewnotes page, "vLLM: preallocated stacked
+ * buffers ..."):
+ *   A_pool    dev [S][r_max][d_in]   pool element type
+ *   B_pool    dev [S][d_out][r_max]  pool element type
+ *   rank_dev  dev int32 [S]          true rank per slot, 0 = empty
+ *   scale_dev dev float [S]          alpha_s / r_s per slot, 0 for empty
+ * Slot 0 stays rank 0, scale 0 for the pool's lifetime.
+ * Synchronises `stream`. Errors: LORA_EINVAL (S < 2, r_max < 1, d_in < 8 or
+ * not a multiple of 8, d_out < 1, unknown dtype, null pointer), LORA_EHIP.
+ */
+int lora_pool_create(lora_pool** out, int S, int r_max, int d_in, int d_out, int dtype,
+                     void* A_pool, void* B_pool, int32_t* rank_dev, float* scale_dev, void* stream);
+
+/* Release the host handle and its status word (not the caller's buffers). */
+void lora_pool_destroy(lora_pool* pool);
+
+/*
+ * Install an adapter into `slot`:
+ *   A dev [r][d_in], B dev [d_out][r] (pool element type), scaling alpha / r
+ *   with r the adapter's true rank ("LoRA adapter application at serve
+ *   time", voxlang.org, conventions table: "alpha / rank").
+ * Validates everything before writing anything (shantanugoel page,
+ * AdapterBank.load): slot in [1, S) (slot 0 is never handed out), 1 <= r <=
+ * r_max, non-null pointers, alpha and every weight finite. Then copies A into
+ * rows 0..r-1 of the slot, zeroes rows r..r_max-1, copies B into columns
+ * 0..r-1, zeroes the rest, and sets rank[slot] = r, scale[slot] = alpha / r
+ * (computed in fp32). Reinstalling an occupied slot is allowed: work queued
+ * earlier on `stream` sees the old weights, later work the new ones; the
+ * caller must not let work on another stream read the slot meanwhile.
+ * Synchronises `stream` (cold path). Errors: LORA_EINVAL, LORA_ESLOT,
+ * LORA_ERANK, LORA_ENONFINITE (pool unchanged), LORA_EHIP.
+ */
+int lora_pool_install(lora_pool* pool, int slot, const void* A, const void* B, int r, float alpha,
+                      void* stream);
+
+/* Reset `slot` (1..S-1) to rank 0, scale 0 and zero weights. Synchronises. */
+int lora_pool_clear(lora_pool* pool, int slot, void* stream);
+
+/* Host mirror of a slot's rank (-1 if slot is out of range). */
+int lora_pool_rank(const lora_pool* pool, int slot);
+
+/*
+ * Per-step segment plan, a pure host function (integer work, bit-exact).
+ * It is built once per step and shared by every adapted linear of every
+ * layer ("mstar.engine.resources.lora.pool", LoraAddressing and
+ * LoraLayerDelta); it holds no weights, so reinstalling a slot does not
+ * invalidate it.
+ *   slot_ids     host int32 [T], each in [0, S)
+ *   token_order  host int32 [T]   out: token indices sorted by (slot, index)
+ *   slot_indptr  host int32 [S+1] out: slot_indptr[s] = #tokens with slot < s
+ *   work         host int32 [work_cap][4] out: {slot, first sorted position,
+ *                row count <= LORA_PLAN_ROWS, 0}, covering every segment of a
+ *                slot >= 1 in ascending slot order
+ *   info         out
+ * Stable counting sort: ascending slot, ascending token index within a slot
+ * (the stable sort plus sorted unique of "LoRA serving, embeddings,
+ * rerankers, pooling", section "vLLM: preallocated stacked buffers ...").
+ * Validates every id before writing any output. Errors: LORA_EINVAL (S < 1,
+ * T < 0, null pointer), LORA_ESLOT, LORA_ESPACE (work_cap too small).
+ */
+int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_order, int32_t* slot_indptr,
+              int32_t* work, int work_cap, lora_plan_info* info);
+
+/* Upper bound on the work list length of any plan over T tokens, S slots. */
+int lora_plan_max_items(int T, int S);
+
+/* Device workspace lora_linear and lora_shrink need for T tokens. */
+size_t lora_workspace_bytes(const lora_pool* pool, int T);
+
+/*
+ * y = x W^T + per-row adapter correction, on `stream`, without host sync.
+ *   x            dev [T][d_in]    pool element type
+ *   W            dev [d_out][d_in]
+ *   token_order, slot_indptr, work: dev copies of lora_plan's outputs
+ *   info         host, from the same lora_plan call (info->S == pool S)
+ *   y            dev [T][d_out]   out; overwritten completely, so its prior
+ *                contents never leak into the result (the uninitialised-output
+ *                hazard of "Silent: the wrong adapter, applied correctly",
+ *                mlinterviewnotes page)
+ *   workspace    dev, at least lora_workspace_bytes(pool, T) bytes
+ * Then y += delta for adapter rows only (LoraLayerDelta semantics); rows on
+ * slot 0 and on rank-0 slots are the base output bit for bit. When
+ * info->T_a == 0 no correction kernel is launched. y must not alias x or W.
+ * Errors: LORA_EINVAL, LORA_ESPACE, LORA_EHIP (launch failure). A device
+ * fault surfaces at the caller's next synchronisation.
+ */
+int lora_linear(const lora_pool* pool, const void* x, const void* W, const int32_t* token_order,
+                const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info, void* y,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The shrink alone, for inspection: h dev fp32 [T][r_max] receives
+ * h[t][q] = sum_k x[t,k] A_s[q,k] for q < r_s, and 0 for q >= r_s and for
+ * rows on slot 0 or a rank-0 slot (the "[tokens, r]-shaped" intermediate of
+ * the mlinterviewnotes page, opening section). Same kernels and summation
+ * order as lora_linear. Errors as lora_linear.
+ */
+int lora_shrink(const lora_pool* pool, const void* x, const int32_t* token_order, const int32_t* slot_indptr,
+                const int32_t* work, const lora_plan_info* info, float* h, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * Per-kernel timing, for diagnostics and the benchmark's roofline figures.
+ * Between lora_profile_begin and lora_profile_end, lora_linear and
+ * lora_shrink record a HIP event pair around every kernel they launch, on
+ * the stream it is launched on (not while that stream is being captured
+ * into a graph, and at most max_records kernels). lora_profile_end waits for
+ * the recorded events and writes one entry per kernel name, in first-launch
+ * order, into out[0..cap); *n_out receives the number of names. Profiling
+ * serialises lora_linear calls across threads while it is on.
+ * Errors: LORA_EINVAL (begin while on, end while off, max_records < 8),
+ * LORA_ESPACE (more names than cap), LORA_EHIP.
+ */
+typedef struct lora_kernel_stat {
+    char name[48];
+    int32_t count;
+    double mean_ms, min_ms, max_ms;
+} lora_kernel_stat;
+
+int lora_profile_begin(int max_records);
+int lora_profile_end(lora_kernel_stat* out, int cap, int* n_out);
+
+/* Human-readable name of a status code (static storage). */
+const char* lora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RANK_GEMM_AMD_LORA_H */

@@ -1,0 +1,358 @@
+// C ABI of liblora: argument validation, the pool handle and launch order.
+// Declarations and contracts: include/lora.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/lora.h"
+#include "kernels.h"
+
+struct lora_pool {
+    int S, r_max, d_in, d_out, dtype;
+    void* A;
+    void* B;
+    int32_t* rank_dev;
+    float* scale_dev;
+    int* flag_dev;  // finite-check result of the last install
+    std::vector<int> rank;
+    std::vector<float> scale;
+};
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+inline size_t es_of(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// workspace layout: [shrink partials][GEMM split-K partials]
+inline size_t shrink_part_bytes(const lora_pool* p, int T) {
+    return align256((size_t)lora::kMaxShrinkSplits * T * p->r_max * sizeof(float));
+}
+
+inline size_t gemm_part_bytes(const lora_pool* p, int T) {
+    if (p->dtype != LORA_BF16) return 0;
+    return align256(lora::gemm_bf16_workspace(T, p->d_out, p->d_in));
+}
+
+// Per-kernel timing for diagnostics: HIP event pairs around each kernel on
+// its launch stream, aggregated by kernel name at lora_profile_end.
+struct Profiler final : lora::StageTimer {
+    std::mutex mu;
+    bool on = false;
+    int max_records = 0;
+    struct Rec {
+        const char* name;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> spare;
+    const char* pending = nullptr;
+    hipEvent_t pending_ev = nullptr;
+
+    hipEvent_t take() {
+        if (!spare.empty()) {
+            hipEvent_t e = spare.back();
+            spare.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    void begin(const char* kernel, hipStream_t st) override {
+        pending = kernel;
+        pending_ev = take();
+        if (pending_ev) (void)hipEventRecord(pending_ev, st);
+    }
+    void end(hipStream_t st) override {
+        hipEvent_t b = take();
+        if (!pending_ev || !b) return;
+        (void)hipEventRecord(b, st);
+        recs.push_back({pending, pending_ev, b});
+        pending_ev = nullptr;
+    }
+};
+
+Profiler& profiler() {
+    static Profiler p;
+    return p;
+}
+
+// Timer for a call on `st`, or nullptr when profiling is off, full, or the
+// stream is being captured into a graph.
+lora::StageTimer* timer_for(hipStream_t st) {
+    Profiler& p = profiler();
+    if (!p.on || (int)p.recs.size() + 8 > p.max_records) return nullptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    return &p;
+}
+
+int check_plan(const lora_pool* p, const int32_t* token_order, const int32_t* slot_indptr, const int32_t* work,
+               const lora_plan_info* info) {
+    if (!p || !info) return LORA_EINVAL;
+    if (info->S != p->S || info->T < 0 || info->T_a < 0 || info->T_a > info->T || info->n_items < 0)
+        return LORA_EINVAL;
+    if (info->T > 0 && (!token_order || !slot_indptr)) return LORA_EINVAL;
+    if (info->n_items > 0 && !work) return LORA_EINVAL;
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_status_string(int status) {
+    switch (status) {
+        case LORA_OK: return "ok";
+        case LORA_EINVAL: return "invalid argument";
+        case LORA_ESLOT: return "slot id out of range";
+        case LORA_ERANK: return "rank out of range";
+        case LORA_ENONFINITE: return "non-finite adapter weights or alpha";
+        case LORA_EHIP: return "HIP runtime error";
+        case LORA_ESPACE: return "buffer too small";
+        default: return "unknown status";
+    }
+}
+
+int lora_pool_create(lora_pool** out, int S, int r_max, int d_in, int d_out, int dtype, void* A_pool, void* B_pool,
+                     int32_t* rank_dev, float* scale_dev, void* stream) {
+    if (!out) return LORA_EINVAL;
+    *out = nullptr;
+    if (S < 2 || r_max < 1 || d_in < 8 || d_in % 8 != 0 || d_out < 1) return LORA_EINVAL;
+    if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_EINVAL;
+    if (!A_pool || !B_pool || !rank_dev || !scale_dev) return LORA_EINVAL;
+    lora_pool* p = new (std::nothrow) lora_pool();
+    if (!p) return LORA_EINVAL;
+    p->S = S;
+    p->r_max = r_max;
+    p->d_in = d_in;
+    p->d_out = d_out;
+    p->dtype = dtype;
+    p->A = A_pool;
+    p->B = B_pool;
+    p->rank_dev = rank_dev;
+    p->scale_dev = scale_dev;
+    p->rank.assign(S, 0);
+    p->scale.assign(S, 0.f);
+    hipStream_t st = as_stream(stream);
+    const size_t es = es_of(dtype);
+    bool ok = hipMalloc(&p->flag_dev, sizeof(int)) == hipSuccess;
+    ok = ok && hipMemsetAsync(A_pool, 0, (size_t)S * r_max * d_in * es, st) == hipSuccess;
+    ok = ok && hipMemsetAsync(B_pool, 0, (size_t)S * d_out * r_max * es, st) == hipSuccess;
+    ok = ok && hipMemsetAsync(rank_dev, 0, (size_t)S * sizeof(int32_t), st) == hipSuccess;
+    ok = ok && hipMemsetAsync(scale_dev, 0, (size_t)S * sizeof(float), st) == hipSuccess;
+    ok = ok && hipStreamSynchronize(st) == hipSuccess;
+    if (!ok) {
+        if (p->flag_dev) (void)hipFree(p->flag_dev);
+        delete p;
+        return LORA_EHIP;
+    }
+    *out = p;
+    return LORA_OK;
+}
+
+void lora_pool_destroy(lora_pool* pool) {
+    if (!pool) return;
+    if (pool->flag_dev) (void)hipFree(pool->flag_dev);
+    delete pool;
+}
+
+int lora_pool_rank(const lora_pool* pool, int slot) {
+    if (!pool || slot < 0 || slot >= pool->S) return -1;
+    return pool->rank[slot];
+}
+
+int lora_pool_install(lora_pool* p, int slot, const void* A, const void* B, int r, float alpha, void* stream) {
+    if (!p || !A || !B) return LORA_EINVAL;
+    if (slot < 1 || slot >= p->S) return LORA_ESLOT;
+    if (r < 1 || r > p->r_max) return LORA_ERANK;
+    if (!std::isfinite(alpha)) return LORA_ENONFINITE;
+    const float sc = alpha / (float)r;
+    if (!std::isfinite(sc)) return LORA_ENONFINITE;
+    hipStream_t st = as_stream(stream);
+    int flag = 0;
+    if (hipMemsetAsync(p->flag_dev, 0, sizeof(int), st) != hipSuccess) return LORA_EHIP;
+    if (lora::pool_check_finite(p->dtype, A, (int64_t)r * p->d_in, p->flag_dev, st) != hipSuccess) return LORA_EHIP;
+    if (lora::pool_check_finite(p->dtype, B, (int64_t)p->d_out * r, p->flag_dev, st) != hipSuccess) return LORA_EHIP;
+    if (hipMemcpyAsync(&flag, p->flag_dev, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return LORA_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LORA_EHIP;
+    if (flag) return LORA_ENONFINITE;
+    if (lora::pool_write_slot(p->dtype, p->A, p->B, p->rank_dev, p->scale_dev, slot, A, B, r, sc, p->r_max, p->d_in,
+                              p->d_out, st) != hipSuccess)
+        return LORA_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LORA_EHIP;
+    p->rank[slot] = r;
+    p->scale[slot] = sc;
+    return LORA_OK;
+}
+
+int lora_pool_clear(lora_pool* p, int slot, void* stream) {
+    if (!p) return LORA_EINVAL;
+    if (slot < 1 || slot >= p->S) return LORA_ESLOT;
+    hipStream_t st = as_stream(stream);
+    if (lora::pool_write_slot(p->dtype, p->A, p->B, p->rank_dev, p->scale_dev, slot, nullptr, nullptr, 0, 0.f,
+                              p->r_max, p->d_in, p->d_out, st) != hipSuccess)
+        return LORA_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LORA_EHIP;
+    p->rank[slot] = 0;
+    p->scale[slot] = 0.f;
+    return LORA_OK;
+}
+
+size_t lora_workspace_bytes(const lora_pool* pool, int T) {
+    if (!pool || T < 0) return 0;
+    return shrink_part_bytes(pool, T) + gemm_part_bytes(pool, T);
+}
+
+static int run_shrink(const lora_pool* p, const void* x, const int32_t* token_order, const int32_t* work,
+                      const lora_plan_info* info, float* part, int* ks_out, hipStream_t st, lora::StageTimer* tm) {
+    const int ks = lora::shrink_splits(info->n_items, p->d_in);
+    *ks_out = ks;
+    if (lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, part, ks, info->T,
+                          p->d_in, p->r_max, st, tm) != hipSuccess)
+        return LORA_EHIP;
+    return LORA_OK;
+}
+
+int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t* token_order,
+                const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info, void* y,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_plan(p, token_order, slot_indptr, work, info);
+    if (rc != LORA_OK) return rc;
+    const int T = info->T;
+    if (T == 0) return LORA_OK;
+    if (!x || !W || !y) return LORA_EINVAL;
+    if (y == x || y == W) return LORA_EINVAL;
+    const size_t need = lora_workspace_bytes(p, T);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return LORA_ESPACE;
+    hipStream_t st = as_stream(stream);
+    char* ws = static_cast<char*>(workspace);
+    float* part = reinterpret_cast<float*>(ws);
+    float* gpart = reinterpret_cast<float*>(ws + shrink_part_bytes(p, T));
+
+    std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
+    if (profiler().on) lk.lock();
+    lora::StageTimer* tm = timer_for(st);
+
+    hipError_t e;
+    if (p->dtype == LORA_BF16)
+        e = lora::gemm_bf16((const uint16_t*)x, (const uint16_t*)W, (uint16_t*)y, T, p->d_out, p->d_in, gpart, st,
+                            tm);
+    else
+        e = lora::gemm_f32((const float*)x, (const float*)W, (float*)y, T, p->d_out, p->d_in, st, tm);
+    if (e != hipSuccess) return LORA_EHIP;
+    if (info->T_a == 0 || info->n_items == 0) return LORA_OK;  // no adapter row: y is the base output
+
+    int ks = 1;
+    rc = run_shrink(p, x, token_order, work, info, part, &ks, st, tm);
+    if (rc != LORA_OK) return rc;
+    if (lora::sgmv_expand(p->dtype, part, ks, p->B, p->rank_dev, p->scale_dev, token_order, work, info->n_items, y, T,
+                          p->d_out, p->r_max, st, tm) != hipSuccess)
+        return LORA_EHIP;
+    return LORA_OK;
+}
+
+int lora_shrink(const lora_pool* p, const void* x, const int32_t* token_order, const int32_t* slot_indptr,
+                const int32_t* work, const lora_plan_info* info, float* h, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    int rc = check_plan(p, token_order, slot_indptr, work, info);
+    if (rc != LORA_OK) return rc;
+    const int T = info->T;
+    if (T == 0) return LORA_OK;
+    if (!x || !h) return LORA_EINVAL;
+    const size_t need = lora_workspace_bytes(p, T);
+    if (!workspace || workspace_bytes < need) return LORA_ESPACE;
+    hipStream_t st = as_stream(stream);
+    float* part = static_cast<float*>(workspace);
+    std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
+    if (profiler().on) lk.lock();
+    lora::StageTimer* tm = timer_for(st);
+    int ks = 1;
+    if (info->n_items > 0) {
+        rc = run_shrink(p, x, token_order, work, info, part, &ks, st, tm);
+        if (rc != LORA_OK) return rc;
+    }
+    if (lora::shrink_to_h(part, ks, p->rank_dev, token_order, slot_indptr, p->S, h, T, p->r_max, st, tm) !=
+        hipSuccess)
+        return LORA_EHIP;
+    return LORA_OK;
+}
+
+int lora_profile_begin(int max_records) {
+    if (max_records < 8) return LORA_EINVAL;
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (p.on) return LORA_EINVAL;
+    for (auto& r : p.recs) {
+        p.spare.push_back(r.a);
+        p.spare.push_back(r.b);
+    }
+    p.recs.clear();
+    p.recs.reserve(max_records);
+    p.max_records = max_records;
+    p.on = true;
+    return LORA_OK;
+}
+
+int lora_profile_end(lora_kernel_stat* out, int cap, int* n_out) {
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.on) return LORA_EINVAL;
+    p.on = false;
+    struct Acc {
+        int n = 0;
+        double sum = 0, mn = 1e30, mx = 0;
+    };
+    std::map<std::string, Acc> acc;
+    std::vector<std::string> order;
+    int rc = LORA_OK;
+    for (auto& r : p.recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+            rc = LORA_EHIP;
+            continue;
+        }
+        auto it = acc.find(r.name);
+        if (it == acc.end()) {
+            order.push_back(r.name);
+            it = acc.emplace(r.name, Acc{}).first;
+        }
+        Acc& a = it->second;
+        ++a.n;
+        a.sum += ms;
+        a.mn = ms < a.mn ? ms : a.mn;
+        a.mx = ms > a.mx ? ms : a.mx;
+    }
+    for (auto& r : p.recs) {
+        p.spare.push_back(r.a);
+        p.spare.push_back(r.b);
+    }
+    p.recs.clear();
+    int n = 0;
+    for (const auto& name : order) {
+        if (out && n < cap) {
+            const Acc& a = acc[name];
+            std::memset(&out[n], 0, sizeof(out[n]));
+            std::strncpy(out[n].name, name.c_str(), sizeof(out[n].name) - 1);
+            out[n].count = a.n;
+            out[n].mean_ms = a.sum / a.n;
+            out[n].min_ms = a.mn;
+            out[n].max_ms = a.mx;
+        }
+        ++n;
+    }
+    if (n_out) *n_out = n;
+    if (rc == LORA_OK && out && n > cap) rc = LORA_ESPACE;
+    return rc;
+}
+
+}  // extern "C"

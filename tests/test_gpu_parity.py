@@ -1,0 +1,270 @@
+"""GPU parity: liblora (through its C ABI) against the fp64 CPU oracle.
+
+Tolerances: max|y - y_ref| / max|y_ref| <= 1e-5 for fp32 pools and <= 2e-2
+for bf16 pools, plus a per-element bound derived from the arithmetic (fp32
+accumulation, at most two bf16 roundings of y). The plan is compared bit for
+bit; rows on slot 0 must equal the base output bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_gemm_amd import lora
+from rank_gemm_amd.inputs import make_config, make_custom
+
+from gpu_util import (TOL, build_pool, check_close, oracle_pair, oracle_rows, rel_err, run_layer, sample_rows,
+                      to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    lora.lib()
+    yield
+
+
+# ------------------------------------------------------------------ configs --
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_config_full_rows(cfg):
+    w = make_config(cfg)
+    for proj in w.projections:
+        y, _, p = run_layer(w, proj)
+        order, indptr, _ = oracle.plan(w.slot_ids, w.S)
+        np.testing.assert_array_equal(p.token_order, order)
+        np.testing.assert_array_equal(p.slot_indptr, indptr)
+        ref, base = oracle_pair(w, proj)
+        check_close(to_f64(y), ref, w.dtype, f"config {cfg} {proj.name}", base)
+
+
+@pytest.mark.parametrize("cfg,n_rows", [(3, 40), (5, 48)])
+def test_config_sampled_rows(cfg, n_rows):
+    """Full-size configs in the benchmark's launch configuration, checked on
+    segment-boundary rows plus seeded random rows."""
+    w = make_config(cfg)
+    rows = sample_rows(w.slot_ids, n_rows, seed=cfg)
+    for proj in w.projections:
+        y, _, _ = run_layer(w, proj)
+        yh = to_f64(y)
+        ref, base = oracle_pair(w, proj, rows=rows)
+        check_close(yh[rows], ref, w.dtype, f"config {cfg} {proj.name} ({len(rows)} rows)", base)
+        assert np.isfinite(yh).all()
+
+
+def test_decode_layers_sampled():
+    """The benchmark's decode step draws one weight set per layer (same slot
+    structure); check two of its layers."""
+    for layer in (1, 31):
+        w = make_config(2, layer=layer)
+        proj = w.projections[0]
+        y, _, _ = run_layer(w, proj)
+        ref, base = oracle_pair(w, proj)
+        check_close(to_f64(y), ref, w.dtype, f"config 2 layer {layer}", base)
+
+
+# ---------------------------------------------------------------- invariants --
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_slot0_rows_bit_exact(cfg):
+    """Rows on slot 0 equal, bit for bit, the output of the same GEMM with no
+    adapter row in the batch (no correction kernel launched at all)."""
+    w = make_config(cfg)
+    proj = w.projections[0]
+    y_mix, pool, _ = run_layer(w, proj)
+    y_base, _, p0 = run_layer(w, proj, pool=pool, slot_ids=np.zeros_like(w.slot_ids))
+    assert p0.info.T_a == 0
+    base_rows = torch.from_numpy(w.slot_ids == 0).to(y_mix.device)
+    assert base_rows.any()
+    assert torch.equal(y_mix[base_rows].view(torch.int16 if w.dtype == "bf16" else torch.int32),
+                       y_base[base_rows].view(torch.int16 if w.dtype == "bf16" else torch.int32))
+    check_close(to_f64(y_base), oracle_rows(w, proj, slot_ids=np.zeros_like(w.slot_ids)), w.dtype, "base only")
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_shrink_h_diagnostic(cfg):
+    """lora_shrink's fp32 h against the oracle's h (<= 1e-4 relative)."""
+    w = make_config(cfg)
+    proj = w.projections[0]
+    pool = build_pool(w, proj)
+    p = lora.plan(w.slot_ids, w.S)
+    x = lora.to_device(proj.x, w.dtype)
+    h = to_f64(lora.shrink(x, pool, p))
+    _, h_ref = oracle_rows(w, proj, want_h=True)
+    err = rel_err(h, h_ref)
+    print(f"[parity] config {cfg} h rel_err={err:.3e}", flush=True)
+    assert err <= 1e-4
+    assert np.all(h[w.slot_ids == 0] == 0)
+
+
+def test_nan_prefilled_output():
+    """y's prior contents never reach the result (the uninitialised-output
+    hazard of the expand that skips base rows)."""
+    w = make_config(4)
+    proj = w.projections[0]
+    y = torch.full((w.T, proj.d_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y, _, _ = run_layer(w, proj, y=y)
+    yh = to_f64(y)
+    assert np.isfinite(yh).all()
+    ref, base = oracle_pair(w, proj)
+    check_close(yh, ref, w.dtype, "nan-prefilled", base)
+
+
+def test_reinstall_then_reuse_plan():
+    """The plan holds no weights: reinstalling a slot and reusing the plan
+    must follow the new weights (stale-metadata hazard)."""
+    w = make_config(2)
+    proj = w.projections[0]
+    pool = build_pool(w, proj)
+    p = lora.plan(w.slot_ids, w.S)
+    x = lora.to_device(proj.x, w.dtype)
+    W = lora.to_device(proj.W, w.dtype)
+    y1 = to_f64(lora.linear(x, W, pool, p))
+    check_close(y1, oracle_rows(w, proj), w.dtype, "before reinstall")
+    other = make_config(2, layer=7).projections[0]
+    proj.adapters[3] = other.adapters[5]
+    a = proj.adapters[3]
+    pool.install(3, lora.to_device(a.A, w.dtype), lora.to_device(a.B, w.dtype), a.alpha)
+    y2 = to_f64(lora.linear(x, W, pool, p))
+    torch.cuda.synchronize()
+    check_close(y2, oracle_rows(w, proj), w.dtype, "after reinstall")
+    changed = w.slot_ids == 3
+    assert np.all(np.any(y1[changed] != y2[changed], axis=1))
+    np.testing.assert_array_equal(y1[~changed], y2[~changed])
+
+
+def test_clear_slot_gives_base_rows():
+    w = make_config(2)
+    proj = w.projections[0]
+    pool = build_pool(w, proj)
+    pool.clear(4)
+    assert pool.rank(4) == 0
+    del proj.adapters[4]
+    y, _, _ = run_layer(w, proj, pool=pool)
+    check_close(to_f64(y), oracle_rows(w, proj), w.dtype, "cleared slot")
+
+
+# -------------------------------------------------------------- edge shapes --
+EDGE = [
+    # T, d_in, d_out, S, ranks, r_max, dtype
+    (1, 64, 16, 2, [0, 4], 4, "bf16"),
+    (37, 264, 100, 5, [0, 3, 0, 7, 1], 8, "bf16"),      # ragged T, odd d_out, rank-0 slot addressed
+    (100, 512, 1, 4, [0, 16, 5, 2], 16, "bf16"),         # single output column
+    (300, 136, 257, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # r_max > 64, several rank groups
+    (53, 128, 96, 4, [0, 2, 3, 1], 3, "bf16"),           # r_max not a multiple of 4
+    (1000, 1024, 520, 9, [0, 16, 16, 8, 16, 16, 16, 16, 16], 16, "bf16"),  # long segments
+    (37, 264, 100, 5, [0, 3, 0, 7, 1], 8, "f32"),
+    (130, 96, 77, 3, [0, 5, 2], 5, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+def test_edge_shapes(case):
+    T, d_in, d_out, S, ranks, r_max, dtype = EDGE[case]
+    g = np.random.default_rng(100 + case)
+    ids = g.integers(0, S, size=T).astype(np.int32)
+    if case == 5:  # long runs: a few big segments and a block of base rows
+        ids = np.repeat(g.integers(0, S, size=8), 125).astype(np.int32)
+    alphas = [2.0 * r for r in ranks]
+    w = make_custom(200 + case, T, d_in, d_out, S, ranks, alphas, ids, dtype=dtype, r_max=r_max)
+    proj = w.projections[0]
+    y, _, _ = run_layer(w, proj)
+    ref, base = oracle_pair(w, proj)
+    check_close(to_f64(y), ref, dtype, f"edge {EDGE[case]}", base)
+
+
+def test_all_rows_one_adapter_and_empty_T():
+    w = make_custom(7, 64, 256, 128, 3, [0, 8, 0], [0, 16, 0], np.ones(64, np.int32))
+    proj = w.projections[0]
+    y, _, _ = run_layer(w, proj)
+    check_close(to_f64(y), oracle_rows(w, proj), "bf16", "one adapter")
+    pool = build_pool(w, proj)
+    p = lora.plan(np.zeros(0, np.int32), 3)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    W = lora.to_device(proj.W, "bf16")
+    y0 = lora.linear(x, W, pool, p)
+    assert y0.shape == (0, 128)
+
+
+# ------------------------------------------------------------------ install --
+def test_install_validation_leaves_pool_unchanged():
+    w = make_config(2)
+    proj = w.projections[0]
+    pool = build_pool(w, proj)
+    snap = (pool.A.clone(), pool.B.clone(), pool.rank_dev.clone(), pool.scale_dev.clone())
+    a = proj.adapters[1]
+    A = lora.to_device(a.A, "bf16")
+    B = lora.to_device(a.B, "bf16")
+    with pytest.raises(lora.LoraError) as e:
+        pool.install(0, A, B, a.alpha)
+    assert e.value.status == lora.LORA_ESLOT
+    with pytest.raises(lora.LoraError) as e:
+        pool.install(9, A, B, a.alpha)
+    assert e.value.status == lora.LORA_ESLOT
+    big = torch.zeros((17, 4096), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lora.LoraError) as e:
+        pool.install(2, big, torch.zeros((4096, 17), dtype=torch.bfloat16, device="cuda"), 1.0)
+    assert e.value.status == lora.LORA_ERANK
+    bad = A.clone()
+    bad[3, 100] = float("nan")
+    with pytest.raises(lora.LoraError) as e:
+        pool.install(2, bad, B, a.alpha)
+    assert e.value.status == lora.LORA_ENONFINITE
+    badb = B.clone()
+    badb[4000, 15] = float("inf")
+    with pytest.raises(lora.LoraError) as e:
+        pool.install(2, A, badb, a.alpha)
+    assert e.value.status == lora.LORA_ENONFINITE
+    with pytest.raises(lora.LoraError) as e:
+        pool.install(2, A, B, float("inf"))
+    assert e.value.status == lora.LORA_ENONFINITE
+    torch.cuda.synchronize()
+    for before, after in zip(snap, (pool.A, pool.B, pool.rank_dev, pool.scale_dev)):
+        assert torch.equal(before.view(torch.uint8), after.view(torch.uint8))
+
+
+def test_pool_layout_and_slot0():
+    """Pool layout after install: A rows past r and B columns past r are zero,
+    rank and scale = alpha / r; slot 0 stays rank 0, scale 0, all zero."""
+    w = make_config(4)
+    proj = w.projections[0]
+    pool = build_pool(w, proj)
+    A = pool.A.float().cpu().numpy()
+    B = pool.B.float().cpu().numpy()
+    rk = pool.rank_dev.cpu().numpy()
+    sc = pool.scale_dev.cpu().numpy()
+    assert rk[0] == 0 and sc[0] == 0 and not A[0].any() and not B[0].any()
+    for s, a in proj.adapters.items():
+        assert rk[s] == a.rank and sc[s] == np.float32(a.alpha) / np.float32(a.rank)
+        assert not A[s, a.rank:].any() and not B[s, :, a.rank:].any()
+        from rank_gemm_amd.inputs import bf16_to_f32
+        np.testing.assert_array_equal(A[s, : a.rank], bf16_to_f32(a.A))
+        np.testing.assert_array_equal(B[s, :, : a.rank], bf16_to_f32(a.B))
+
+
+# ------------------------------------------------------------ long context --
+def test_row_offsets_beyond_int32():
+    """T * d_in > 2^31 elements: rows past 524,288 of a 4096-wide x are read
+    and written at 64-bit offsets (the long-context overflow hazard)."""
+    T, d_in, d_out, S = 524_288 + 640, 4096, 32, 3
+    ids = np.zeros(T, np.int32)
+    tail = np.arange(T - 40, T)
+    ids[tail[:20]] = 1
+    ids[tail[20:]] = 2
+    ids[:8] = 2
+    check = np.concatenate([np.arange(8), tail]).astype(np.int32)
+    # small host workload holding only the checked rows
+    sub = make_custom(9, len(check), d_in, d_out, S, [0, 16, 8], [0, 32, 16], ids[check])
+    proj = sub.projections[0]
+    pool = build_pool(sub, proj)
+    x = torch.zeros((T, d_in), dtype=torch.bfloat16, device="cuda")
+    x[torch.from_numpy(check).long().cuda()] = lora.to_device(proj.x, "bf16")
+    W = lora.to_device(proj.W, "bf16")
+    p = lora.plan(ids, S)
+    y = lora.linear(x, W, pool, p)
+    torch.cuda.synchronize()
+    yh = to_f64(y[torch.from_numpy(check).long().cuda()])
+    check_close(yh, oracle_rows(sub, proj), "bf16", "rows beyond int32 offsets")
+    del x, y
+    torch.cuda.empty_cache()
