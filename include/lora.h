@@ -55,6 +55,9 @@ extern "C" {
 /* rows per work item of the plan (one 16-row matrix-core tile) */
 #define LORA_PLAN_ROWS 16
 
+/* largest r_max a pool may have */
+#define LORA_MAX_RANK 1024
+
 typedef struct lora_pool lora_pool;
 
 /* Summary of one plan; filled by lora_plan, read by lora_linear. */
@@ -78,8 +81,9 @@ typedef struct lora_plan_info {
  *   rank_dev  dev int32 [S]          true rank per slot, 0 = empty
  *   scale_dev dev float [S]          alpha_s / r_s per slot, 0 for empty
  * Slot 0 stays rank 0, scale 0 for the pool's lifetime.
- * Synchronises `stream`. Errors: LORA_EINVAL (S < 2, r_max < 1, d_in < 8 or
- * not a multiple of 8, d_out < 1, unknown dtype, null pointer), LORA_EHIP.
+ * Synchronises `stream`. Errors: LORA_EINVAL (S < 2, r_max outside
+ * [1, LORA_MAX_RANK], d_in < 8 or not a multiple of 8, d_out < 1, unknown
+ * dtype, null pointer), LORA_EHIP.
  */
 int lora_pool_create(lora_pool** out, int S, int r_max, int d_in, int d_out, int dtype,
                      void* A_pool, void* B_pool, int32_t* rank_dev, float* scale_dev, void* stream);
@@ -150,7 +154,10 @@ size_t lora_workspace_bytes(const lora_pool* pool, int T);
  *                contents never leak into the result (the uninitialised-output
  *                hazard of "Silent: the wrong adapter, applied correctly",
  *                mlinterviewnotes page)
- *   workspace    dev, at least lora_workspace_bytes(pool, T) bytes
+ *   workspace    dev, at least lora_workspace_bytes(pool, T) bytes (bf16 pools
+ *                always need it; fp32 pools only when info->T_a > 0); holds
+ *                partial products and the shrink output between kernels, so
+ *                calls that may overlap need separate workspaces
  * Then y += delta for adapter rows only (LoraLayerDelta semantics); rows on
  * slot 0 and on rank-0 slots are the base output bit for bit. When
  * info->T_a == 0 no correction kernel is launched. y must not alias x or W.
@@ -165,8 +172,10 @@ int lora_linear(const lora_pool* pool, const void* x, const void* W, const int32
  * The shrink alone, for inspection: h dev fp32 [T][r_max] receives
  * h[t][q] = sum_k x[t,k] A_s[q,k] for q < r_s, and 0 for q >= r_s and for
  * rows on slot 0 or a rank-0 slot (the "[tokens, r]-shaped" intermediate of
- * the mlinterviewnotes page, opening section). Same kernels and summation
- * order as lora_linear. Errors as lora_linear.
+ * the mlinterviewnotes page, opening section). It uses the same per-item
+ * shrink code as lora_linear over the whole K range (lora_linear may split K
+ * and add the splits, so the two agree to fp32 rounding, not bit for bit).
+ * Errors as lora_linear.
  */
 int lora_shrink(const lora_pool* pool, const void* x, const int32_t* token_order, const int32_t* slot_indptr,
                 const int32_t* work, const lora_plan_info* info, float* h, void* workspace,

@@ -32,14 +32,12 @@ inline size_t es_of(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-// workspace layout: [shrink partials][GEMM split-K partials]
-inline size_t shrink_part_bytes(const lora_pool* p, int T) {
-    return align256((size_t)lora::kMaxShrinkSplits * T * p->r_max * sizeof(float));
-}
-
-inline size_t gemm_part_bytes(const lora_pool* p, int T) {
-    if (p->dtype != LORA_BF16) return 0;
-    return align256(lora::gemm_bf16_workspace(T, p->d_out, p->d_in));
+// workspace: the bf16 path's partial products and h; the fp32 path's h
+inline size_t h_bytes(const lora_pool* p, int T) {
+    const size_t h = align256((size_t)T * p->r_max * sizeof(float));
+    if (p->dtype != LORA_BF16) return h;
+    const size_t g = lora::gemm_bf16_workspace(T, p->d_out, p->d_in, p->r_max);
+    return g > h ? g : h;
 }
 
 // Per-kernel timing for diagnostics: HIP event pairs around each kernel on
@@ -54,8 +52,6 @@ struct Profiler final : lora::StageTimer {
     };
     std::vector<Rec> recs;
     std::vector<hipEvent_t> spare;
-    const char* pending = nullptr;
-    hipEvent_t pending_ev = nullptr;
 
     hipEvent_t take() {
         if (!spare.empty()) {
@@ -67,17 +63,14 @@ struct Profiler final : lora::StageTimer {
         if (hipEventCreate(&e) != hipSuccess) return nullptr;
         return e;
     }
-    void begin(const char* kernel, hipStream_t st) override {
-        pending = kernel;
-        pending_ev = take();
-        if (pending_ev) (void)hipEventRecord(pending_ev, st);
-    }
-    void end(hipStream_t st) override {
-        hipEvent_t b = take();
-        if (!pending_ev || !b) return;
-        (void)hipEventRecord(b, st);
-        recs.push_back({pending, pending_ev, b});
-        pending_ev = nullptr;
+    bool pair(const char* kernel, hipEvent_t* start, hipEvent_t* stop) override {
+        if ((int)recs.size() >= max_records) return false;
+        hipEvent_t a = take(), b = take();
+        if (!a || !b) return false;
+        recs.push_back({kernel, a, b});
+        *start = a;
+        *stop = b;
+        return true;
     }
 };
 
@@ -90,7 +83,7 @@ Profiler& profiler() {
 // stream is being captured into a graph.
 lora::StageTimer* timer_for(hipStream_t st) {
     Profiler& p = profiler();
-    if (!p.on || (int)p.recs.size() + 8 > p.max_records) return nullptr;
+    if (!p.on || (int)p.recs.size() >= p.max_records) return nullptr;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
     return &p;
@@ -127,7 +120,7 @@ int lora_pool_create(lora_pool** out, int S, int r_max, int d_in, int d_out, int
                      int32_t* rank_dev, float* scale_dev, void* stream) {
     if (!out) return LORA_EINVAL;
     *out = nullptr;
-    if (S < 2 || r_max < 1 || d_in < 8 || d_in % 8 != 0 || d_out < 1) return LORA_EINVAL;
+    if (S < 2 || r_max < 1 || r_max > LORA_MAX_RANK || d_in < 8 || d_in % 8 != 0 || d_out < 1) return LORA_EINVAL;
     if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_EINVAL;
     if (!A_pool || !B_pool || !rank_dev || !scale_dev) return LORA_EINVAL;
     lora_pool* p = new (std::nothrow) lora_pool();
@@ -210,17 +203,7 @@ int lora_pool_clear(lora_pool* p, int slot, void* stream) {
 
 size_t lora_workspace_bytes(const lora_pool* pool, int T) {
     if (!pool || T < 0) return 0;
-    return shrink_part_bytes(pool, T) + gemm_part_bytes(pool, T);
-}
-
-static int run_shrink(const lora_pool* p, const void* x, const int32_t* token_order, const int32_t* work,
-                      const lora_plan_info* info, float* part, int* ks_out, hipStream_t st, lora::StageTimer* tm) {
-    const int ks = lora::shrink_splits(info->n_items, p->d_in);
-    *ks_out = ks;
-    if (lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, part, ks, info->T,
-                          p->d_in, p->r_max, st, tm) != hipSuccess)
-        return LORA_EHIP;
-    return LORA_OK;
+    return h_bytes(pool, T);
 }
 
 int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t* token_order,
@@ -232,31 +215,31 @@ int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t*
     if (T == 0) return LORA_OK;
     if (!x || !W || !y) return LORA_EINVAL;
     if (y == x || y == W) return LORA_EINVAL;
-    const size_t need = lora_workspace_bytes(p, T);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return LORA_ESPACE;
+    const bool adapters = info->T_a > 0 && info->n_items > 0;
+    if (adapters && (!workspace || workspace_bytes < lora_workspace_bytes(p, T))) return LORA_ESPACE;
     hipStream_t st = as_stream(stream);
-    char* ws = static_cast<char*>(workspace);
-    float* part = reinterpret_cast<float*>(ws);
-    float* gpart = reinterpret_cast<float*>(ws + shrink_part_bytes(p, T));
+    float* h = static_cast<float*>(workspace);
 
     std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
     if (profiler().on) lk.lock();
     lora::StageTimer* tm = timer_for(st);
 
-    hipError_t e;
-    if (p->dtype == LORA_BF16)
-        e = lora::gemm_bf16((const uint16_t*)x, (const uint16_t*)W, (uint16_t*)y, T, p->d_out, p->d_in, gpart, st,
-                            tm);
-    else
-        e = lora::gemm_f32((const float*)x, (const float*)W, (float*)y, T, p->d_out, p->d_in, st, tm);
-    if (e != hipSuccess) return LORA_EHIP;
-    if (info->T_a == 0 || info->n_items == 0) return LORA_OK;  // no adapter row: y is the base output
-
-    int ks = 1;
-    rc = run_shrink(p, x, token_order, work, info, part, &ks, st, tm);
-    if (rc != LORA_OK) return rc;
-    if (lora::sgmv_expand(p->dtype, part, ks, p->B, p->rank_dev, p->scale_dev, token_order, work, info->n_items, y, T,
-                          p->d_out, p->r_max, st, tm) != hipSuccess)
+    if (p->dtype == LORA_BF16) {
+        if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
+        const lora::LinearArgs la{(const uint16_t*)x, (const uint16_t*)W, (uint16_t*)y, T, p->d_out, p->d_in,
+                                  token_order, slot_indptr, work, info->n_items, (const uint16_t*)p->A,
+                                  (const uint16_t*)p->B, p->rank_dev, p->scale_dev, p->S, p->r_max,
+                                  adapters ? 1 : 0, workspace};
+        return lora::lora_forward_bf16(la, st, tm) == hipSuccess ? LORA_OK : LORA_EHIP;
+    }
+    if (lora::gemm_f32((const float*)x, (const float*)W, (float*)y, T, p->d_out, p->d_in, st, tm) != hipSuccess)
+        return LORA_EHIP;
+    if (!adapters) return LORA_OK;  // no adapter row: y is the base output
+    if (lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, h, p->d_in, p->r_max, st,
+                          tm) != hipSuccess)
+        return LORA_EHIP;
+    if (lora::sgmv_expand_f32(h, (const float*)p->B, p->rank_dev, p->scale_dev, token_order, work, info->n_items,
+                              (float*)y, p->d_out, p->r_max, st, tm) != hipSuccess)
         return LORA_EHIP;
     return LORA_OK;
 }
@@ -269,20 +252,16 @@ int lora_shrink(const lora_pool* p, const void* x, const int32_t* token_order, c
     const int T = info->T;
     if (T == 0) return LORA_OK;
     if (!x || !h) return LORA_EINVAL;
-    const size_t need = lora_workspace_bytes(p, T);
-    if (!workspace || workspace_bytes < need) return LORA_ESPACE;
+    if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
     hipStream_t st = as_stream(stream);
-    float* part = static_cast<float*>(workspace);
+    float* hs = static_cast<float*>(workspace);
     std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
     if (profiler().on) lk.lock();
     lora::StageTimer* tm = timer_for(st);
-    int ks = 1;
-    if (info->n_items > 0) {
-        rc = run_shrink(p, x, token_order, work, info, part, &ks, st, tm);
-        if (rc != LORA_OK) return rc;
-    }
-    if (lora::shrink_to_h(part, ks, p->rank_dev, token_order, slot_indptr, p->S, h, T, p->r_max, st, tm) !=
-        hipSuccess)
+    if (info->n_items > 0 && lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, hs,
+                                               p->d_in, p->r_max, st, tm) != hipSuccess)
+        return LORA_EHIP;
+    if (lora::scatter_h(hs, p->rank_dev, token_order, slot_indptr, p->S, h, T, p->r_max, st, tm) != hipSuccess)
         return LORA_EHIP;
     return LORA_OK;
 }

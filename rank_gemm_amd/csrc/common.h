@@ -12,6 +12,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace lora {
 
+// 16 zero bytes in device memory: a masked-off 16-byte load reads from here
+// (the address is selected, not the loaded value, so no load is waited on
+// early and no branch is needed).
+static __device__ const u32x4 kZeros16[1] = {{0, 0, 0, 0}};
+
+__device__ __forceinline__ const u32x4* or_zero(bool ok, const void* p) {
+    return ok ? static_cast<const u32x4*>(p) : kZeros16;
+}
+
 // bf16 bit pattern -> float (exact)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 

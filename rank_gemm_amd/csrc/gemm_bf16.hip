@@ -1,20 +1,178 @@
-// Base GEMM of the LoRA linear on gfx950 matrix cores:
-//   Y[M][N] = bf16( X[M][K] * W[N][K]^T ), fp32 accumulation.
-// Both operands are K-contiguous (x rows, nn.Linear weight rows), so the
-// same LDS path serves both. Macro tiles of BM x BN are computed by 4 waves
-// in a 2 x 2 grid with v_mfma_f32_16x16x32_bf16; K advances 64 at a time
-// through a double-buffered, XOR-swizzled LDS stage.
+// Base GEMM of the LoRA linear on gfx950 matrix cores, with the SGMV expand
+// fused into its epilogue:
+//   y[t_p] = bf16( x[t_p] W^T + scale_s * h[p] B_s^T )   for sorted position p
+// where t_p = token_order[p] and s is the slot whose segment holds p. The base
+// product is the plain GEMM of "LoRA serving, embeddings, rerankers, pooling"
+// (mlinterviewnotes.com, opening section: base GEMM once over the batch, then
+// the per-row indexed low-rank correction); doing the correction in the
+// epilogue writes y once instead of re-reading it.
+//
+// Rows are visited in plan (segment) order, so a 16-row block meets few
+// slots: each slot met adds one more rank-deep product per block, with h
+// (fp32, from the shrink) fed to the matrix cores as bf16 hi + lo halves.
+// Rows on slot 0, or on a rank-0 slot, get no product at all, so their bits
+// equal those of a run with no adapter row.
+//
+// Two paths:
+//  * tiled (prefill-sized T): BM x BN macro tiles, 4 waves in 2 x 2, K in
+//    steps of 64 through a double-buffered, XOR-swizzled LDS stage; the
+//    shrink runs before it as its own kernel.
+//  * split-K (decode-sized T): kernel 1 computes 64 x 64 output tiles over K
+//    splits, gathering x rows into LDS in 128-wide sub-chunks while W is
+//    streamed from HBM straight into registers two sub-chunks ahead; extra
+//    workgroups of the same launch compute the shrink over the same K
+//    splits. Kernel 2 adds the partial products in split order, applies the
+//    expand and rounds once. No workgroup waits on another.
 #include "common.h"
 #include "kernels.h"
+#include "shrink.h"
 
 namespace lora {
 
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
+struct Fuse {
+    const int32_t* token_order;  // sorted position -> token row
+    const int32_t* slot_indptr;  // [S+1]
+    const float* h;              // h_splits planes of [T][r_max], sorted positions, unscaled
+    const uint16_t* B_pool;      // [S][N][r_max]
+    const int32_t* rank;
+    const float* scale;
+    int S, r_max;
+    int h_splits;     // planes of h to add (1 when the shrink produced final h)
+    int64_t h_plane;  // elements per plane
+    int adapters;     // 0: no adapter row in the batch, skip the correction
+    const uint16_t* ext;  // tiled path: scaled h as bf16 hi / lo rows [T][2][rp], or null
+    int rp;               // r_max rounded up to 8
+};
+
+// Slot metadata (segment offsets, ranks, scales) staged in LDS at kernel
+// start, so the epilogue's slot walk does not chain global-memory latencies.
+// Pools with more than kMetaSlots slots read it from global memory instead.
+constexpr int kMetaSlots = 1024;
+struct SlotMeta {
+    int indptr[kMetaSlots + 1];
+    int rank[kMetaSlots];
+    float scale[kMetaSlots];
+};
+
+struct MetaView {
+    const int* indptr;
+    const int* rank;
+    const float* scale;
+};
+
+// Cooperative copy by every thread of the block; call before a barrier.
+__device__ __forceinline__ MetaView stage_meta(const Fuse& f, SlotMeta* sm) {
+    if (!f.adapters || f.S > kMetaSlots) return MetaView{f.slot_indptr, f.rank, f.scale};
+    for (int i = threadIdx.x; i <= f.S; i += blockDim.x) {
+        sm->indptr[i] = f.slot_indptr[i];
+        if (i < f.S) {
+            sm->rank[i] = f.rank[i];
+            sm->scale[i] = f.scale[i];
+        }
+    }
+    return MetaView{sm->indptr, sm->rank, sm->scale};
+}
+
 // 16-byte LDS chunk of (row, logical chunk c in 0..7). The XOR spreads the
 // 16 rows one MFMA operand read touches over distinct banks.
 __device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
+
+// Last slot s with slot_indptr[s] <= p (the slot whose segment holds p).
+__device__ __forceinline__ int slot_of(const int* indptr, int S, int p) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (indptr[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// acc[i][j] covers sorted rows p0 + 16 i + (4 (lane/16) + e) and columns
+// n0 + 16 j + lane % 16. Adds scale_s * h[p] . B_s[n] for every adapter row.
+template <int FM, int FN>
+__device__ __forceinline__ void fused_expand(f32x4 (&acc)[FM][FN], const Fuse& f, const MetaView& mv, int p0,
+                                             int n0, int M, int N, int lane) {
+    const int pend = min(M, p0 + FM * 16);
+    if (!f.adapters || p0 >= pend) return;
+    const int col = lane & 15, qg = lane >> 4;
+    const bool vec = (f.r_max & 3) == 0;
+    for (int s = slot_of(mv.indptr, f.S, p0); s < f.S; ++s) {
+        const int sb = mv.indptr[s], se = mv.indptr[s + 1];
+        if (sb >= pend) break;
+        const int r = mv.rank[s];
+        if (s == 0 || r == 0 || se <= p0 || se <= sb) continue;
+        const float sc = mv.scale[s];
+        const uint16_t* bs = f.B_pool + (int64_t)s * N * f.r_max;
+        const int nq = (r + 15) >> 4;
+        for (int qs = 0; qs < nq; ++qs) {
+            const int q = qs * 16 + qg * 4;
+            u32x2 bfr[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + j * 16 + col;
+                const uint16_t* src = bs + (int64_t)n * f.r_max + q;
+                if (vec) {  // B is zero past r inside the padded row
+                    bfr[j] = (n < N && q < r) ? *(const u32x2*)src : u32x2{0, 0};
+                } else {
+                    uint16_t e4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) e4[e] = (n < N && q + e < r) ? src[e] : uint16_t(0);
+                    bfr[j] = u32x2{uint32_t(e4[0]) | (uint32_t(e4[1]) << 16),
+                                   uint32_t(e4[2]) | (uint32_t(e4[3]) << 16)};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int bb = p0 + i * 16;
+                if (bb >= se || bb + 16 <= sb) continue;  // block outside the segment (uniform)
+                const int p = bb + col;                   // this lane's row of the A operand
+                const bool in = p >= sb && p < se;
+                float hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = 0.f;
+                    if (in && q + e < r) {
+                        const float* hp = f.h + (int64_t)p * f.r_max + q + e;
+                        for (int z = 0; z < f.h_splits; ++z) v += hp[z * f.h_plane];
+                        v *= sc;
+                    }
+                    hi[e] = bf16_to_f32(f32_to_bf16(v));
+                    lo[e] = v - hi[e];
+                }
+                const u32x2 ahi{pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+                const u32x2 alo{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    acc[i][j] = mfma16x16x16(ahi, bfr[j], acc[i][j]);
+                    acc[i][j] = mfma16x16x16(alo, bfr[j], acc[i][j]);
+                }
+            }
+        }
+    }
+}
+
+// Round and store: y[token_order[p]][n] for the rows and columns of acc.
+template <int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], uint16_t* __restrict__ Y,
+                                           const int32_t* __restrict__ token_order, int p0, int n0, int M, int N,
+                                           int lane) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int p = p0 + i * 16 + (lane >> 4) * 4 + e;
+            if (p >= M) continue;
+            uint16_t* yr = Y + (int64_t)token_order[p] * N;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + j * 16 + (lane & 15);
+                if (n < N) yr[n] = f32_to_bf16(acc[i][j][e]);
+            }
+        }
+}
 
 // Map a linear block id to (tile_m, tile_n). Consecutive ids go round-robin
 // over the 8 XCDs, so ids are first regrouped so that each XCD owns one
@@ -35,43 +193,107 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     tn = in / gsize;
 }
 
-template <int BM, int BN, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
-                                                                const uint16_t* __restrict__ W,
-                                                                void* __restrict__ out, int M, int N, int K,
-                                                                int k_chunk, int tiles_m, int tiles_n) {
+// The expand as extra K steps of the tiled GEMM. For each slot s whose
+// segment meets the tile's rows [m0, mend) the K dimension is extended by
+// 2 rp (rp = r_max rounded up to 8): the A operand of row p is its ext row
+// [bf16 hi of scale_s h | lo remainder] (zero for rows of other segments),
+// the B operand of column n is [B_s[n] | B_s[n]], so the products add
+// scale_s h . B_s. The extension is walked in steps of 64.
+struct ExtraStep {
+    int s, sb, se, r, t;
+};
+
+// Number of extra steps (e < 0) or the decoding of step e.
+__device__ __forceinline__ int extra_steps(const MetaView& mv, const Fuse& f, int m0, int mend, int e,
+                                           ExtraStep* out) {
+    int n = 0;
+    for (int s = slot_of(mv.indptr, f.S, m0); s < f.S; ++s) {
+        const int sb = mv.indptr[s], se = mv.indptr[s + 1];
+        if (sb >= mend) break;
+        const int r = mv.rank[s];
+        if (s == 0 || r == 0 || se <= m0 || se <= sb) continue;
+        const int k = (2 * f.rp + 63) >> 6;
+        if (e >= 0 && e < n + k) {
+            *out = ExtraStep{s, sb, se, r, e - n};
+            return e;
+        }
+        n += k;
+    }
+    return n;
+}
+
+// ------------------------------------------------------------------ tiled --
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const uint16_t* __restrict__ X,
+                                                                 const uint16_t* __restrict__ W,
+                                                                 uint16_t* __restrict__ Y, int M, int N, int K,
+                                                                 int tiles_m, int tiles_n, Fuse f) {
     constexpr int WTM = BM / 2, WTN = BN / 2;
     constexpr int FM = WTM / 16, FN = WTN / 16;
     constexpr int AC = BM * 8 / kThreads;  // 16-byte chunks per thread per stage
     constexpr int BC = BN * 8 / kThreads;
     __shared__ u32x4 lds[2 * (BM + BN) * 8];
+    __shared__ SlotMeta meta;
     u32x4* As = lds;
     u32x4* Bs = lds + 2 * BM * 8;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    const MetaView mv = stage_meta(f, &meta);  // ordered by the main loop's barriers
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int kz = blockIdx.y;
-    const int kbeg = kz * k_chunk;
-    const int kend = min(K, kbeg + k_chunk);
-    const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
+    const int nk = (K + kBK - 1) / kBK;
 
     const int lc = tid & 7, lr = tid >> 3;
+    const uint16_t* xrow[AC];  // gathered x rows of this thread's chunks (clamped; xok masks)
+    bool xok[AC];
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+        const int p = m0 + lr + 32 * i;
+        xok[i] = p < M;
+        xrow[i] = X + (int64_t)f.token_order[min(p, M - 1)] * K;
+    }
+    const int mend = min(M, m0 + BM);
+    // interior tiles (the uniform common case) load without masks; elsewhere
+    // a masked-off chunk reads zeros (or_zero selects the address)
+    const bool interior = m0 + BM <= M && n0 + BN <= N && (K % kBK) == 0;
+    const uint16_t* wtile = W + (int64_t)n0 * K;
     u32x4 ra[AC], rb[BC];
-    auto gload = [&](int k0) {
-        const int kk = k0 + lc * 8;
-        const bool kin = kk < kend;  // K % 8 == 0: a chunk is fully in or out
+    auto gload = [&](int it) {
+        if (it < nk) {
+            const int kk = it * kBK + lc * 8;
+            if (interior) {
+#pragma unroll
+                for (int i = 0; i < AC; ++i) ra[i] = *(const u32x4*)(xrow[i] + kk);
+#pragma unroll
+                for (int i = 0; i < BC; ++i) rb[i] = *(const u32x4*)(wtile + (int64_t)(lr + 32 * i) * K + kk);
+                return;
+            }
+            const bool kin = kk < K;  // K % 8 == 0: a chunk is fully in or out
+#pragma unroll
+            for (int i = 0; i < AC; ++i) ra[i] = *or_zero(kin && xok[i], xrow[i] + kk);
+#pragma unroll
+            for (int i = 0; i < BC; ++i) {
+                const int r = n0 + lr + 32 * i;
+                rb[i] = *or_zero(kin && r < N, W + (int64_t)r * K + kk);
+            }
+            return;
+        }
+        ExtraStep x{};
+        extra_steps(mv, f, m0, mend, it - nk, &x);
+        const int k0 = x.t * 64 + lc * 8;       // position in the 2 rp extension
+        const int q0 = k0 < f.rp ? k0 : k0 - f.rp;  // rank of the chunk (rp % 8 == 0)
+        const bool qin = k0 < 2 * f.rp && q0 < x.r;
 #pragma unroll
         for (int i = 0; i < AC; ++i) {
-            const int r = m0 + lr + 32 * i;
-            ra[i] = (kin && r < M) ? *(const u32x4*)(X + (int64_t)r * K + kk) : u32x4{0, 0, 0, 0};
+            const int p = m0 + lr + 32 * i;
+            ra[i] = *or_zero(qin && p >= x.sb && p < x.se, f.ext + (int64_t)p * 2 * f.rp + k0);
         }
 #pragma unroll
         for (int i = 0; i < BC; ++i) {
-            const int r = n0 + lr + 32 * i;
-            rb[i] = (kin && r < N) ? *(const u32x4*)(W + (int64_t)r * K + kk) : u32x4{0, 0, 0, 0};
+            const int n = n0 + lr + 32 * i;
+            rb[i] = *or_zero(qin && n < N, f.B_pool + ((int64_t)x.s * N + n) * f.r_max + q0);
         }
     };
     auto sstore = [&](int buf) {
@@ -87,14 +309,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const uint16_t* 
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (nk > 0) {
-        gload(kbeg);
-        sstore(0);
-    }
+    gload(0);
+    sstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
+    // the slot metadata is in LDS now: count the expand's extra K steps
+    const int nt = nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr) : 0);
+    for (int kt = 0; kt < nt; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kbeg + (kt + 1) * kBK);
+        if (kt + 1 < nt) gload(kt + 1);
         const u32x4* Ab = As + buf * BM * 8;
         const u32x4* Bb = Bs + buf * BN * 8;
 #pragma unroll
@@ -110,96 +332,342 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const uint16_t* 
 #pragma unroll
                 for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bfg[j], acc[i][j]);
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
+        if (kt + 1 < nt) sstore(buf ^ 1);
         __syncthreads();
     }
 
-    // lane holds rows 4*(lane/16)+e, column lane%16 of every 16x16 block
+    const int p0 = m0 + wm * WTM, nb = n0 + wn * WTN;
+    if (!f.ext) fused_expand<FM, FN>(acc, f, mv, p0, nb, M, N, lane);
+    store_tile<FM, FN>(acc, Y, f.token_order, p0, nb, M, N, lane);
+}
+
+// -------------------------------------------------------------- split-K --
+// LDS chunk (row, c) for sub-chunks of 128 k: 16 chunks per row.
+__device__ __forceinline__ int swz16(int row, int c) { return row * 16 + (c ^ (row & 15)); }
+
+struct SplitArgs {
+    const uint16_t* X;
+    const uint16_t* W;
+    float* part_y;  // [ks][n_mt][n_nt][16 fragments][64 lanes] f32x4
+    int M, N, K, n_mt, n_nt, ks;
+    // shrink workgroups (the first n_items * ks blocks)
+    const uint16_t* A_pool;
+    const int32_t* rank;
+    const int32_t* token_order;
+    const Item* work;
+    int n_items, r_max;
+    float* part_h;  // [ks][M][r_max]
+};
+
+// grid: n_items * ks shrink blocks, then n_mt * n_nt * ks GEMM blocks.
+// Wave w of a GEMM block owns columns n0 + 16 w .. + 15 of a 64 x 64 tile.
+template <int NSUB>
+__global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
+    __shared__ u32x4 lds[2 * 64 * 16];  // two 64 x 128 bf16 stages of x (32 KB)
+    constexpr int KC = NSUB * 128;
+    const int n_shrink = a.n_items * a.ks;
+    if ((int)blockIdx.x < n_shrink) {
+        const int item = blockIdx.x % a.n_items, kz = blockIdx.x / a.n_items;
+        const Item it = a.work[item];
+        const int r = a.rank[it.slot];
+        if (r == 0) return;
+        const int kbeg = kz * KC, kend = min(a.K, kbeg + KC);
+        const ShrinkOut out{a.part_h + (int64_t)kz * a.M * a.r_max, nullptr, 0, 0.f};
+        shrink_item<4>(a.X, a.A_pool, r, a.token_order, it, out, a.K, kbeg, kend, a.r_max,
+                       reinterpret_cast<f32x4*>(lds));
+        return;
+    }
+    const int g = blockIdx.x - n_shrink;
+    const int tiles = a.n_mt * a.n_nt;
+    const int kz = g / tiles, t = g - kz * tiles;
+    const int mt = t / a.n_nt, nt = t - mt * a.n_nt;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    const int m0 = mt * 64, n = nt * 64 + wave * 16 + col;
+    const int kbeg = kz * KC;
+    const int K = a.K;
+
+    // interior tiles (every row, column and k of the split inside the
+    // matrices: the uniform common case) load without masks; edge tiles mask
+    // out-of-range elements to zero
+    const bool interior = m0 + 64 <= a.M && nt * 64 + 64 <= a.N && kbeg + KC <= K;
+    const bool wok = n < a.N;
+    const uint16_t* wrow = a.W + (int64_t)min(n, a.N - 1) * K;
+    // x staging: 16 threads per row (256 B), 16 rows per pass, 4 passes
+    const int xr = tid >> 4, xc = tid & 15;
+    const uint16_t* xrow[4];
+    bool xok[4];
+    u32x4 xreg[4];
+    auto xload = [&](int j) {
+        const int kk = kbeg + j * 128 + xc * 8;
+        if (interior) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < 4; ++i) xreg[i] = *(const u32x4*)(xrow[i] + kk);
+        } else {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * WTN + j * 16 + (lane & 15);
+            for (int i = 0; i < 4; ++i) xreg[i] = *or_zero(xok[i] && kk < K, xrow[i] + kk);
+        }
+    };
+    auto xstore = [&](int b) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + e;
-                if (row < M && col < N) {
-                    if constexpr (SPLIT)
-                        ((float*)out)[((int64_t)kz * M + row) * N + col] = acc[i][j][e];
-                    else
-                        ((uint16_t*)out)[(int64_t)row * N + col] = f32_to_bf16(acc[i][j][e]);
-                }
+        for (int i = 0; i < 4; ++i) lds[b * 1024 + swz16(xr + 16 * i, xc)] = xreg[i];
+    };
+    u32x4 wreg[3][4];
+    auto wload = [&](int j, int slot) {
+        if (interior) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) wreg[slot][u] = *(const u32x4*)(wrow + kbeg + j * 128 + u * 32 + kg * 8);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kk = kbeg + j * 128 + u * 32 + kg * 8;
+                wreg[slot][u] = *or_zero(wok && kk < K, wrow + kk);
             }
         }
+    };
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // W does not depend on the plan: start streaming it before the gather
+    wload(0, 0);
+    if (NSUB > 1) wload(1, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = m0 + xr + 16 * i;
+        xok[i] = p < a.M;
+        xrow[i] = a.X + (int64_t)a.token_order[min(p, a.M - 1)] * K;
+    }
+    xload(0);
+    xstore(0);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+        if (j + 1 < NSUB) xload(j + 1);
+        if (j + 2 < NSUB) wload(j + 2, (j + 2) % 3);
+        u32x4 xf[4][4];  // all of this sub-chunk's x fragments, read before the products
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xf[u][i] = lds[(j & 1) * 1024 + swz16(i * 16 + col, u * 4 + kg)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = mfma16x16x32(xf[u][i], wreg[j % 3][u], acc[i]);
+        if (j + 1 < NSUB) xstore((j + 1) & 1);
+        __syncthreads();
+    }
+    f32x4* out = reinterpret_cast<f32x4*>(a.part_y) + ((int64_t)(kz * a.n_mt + mt) * a.n_nt + nt) * 16 * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[(i * 4 + wave) * 64 + lane] = acc[i];
 }
 
-// Sum the K-split partials in split order and round once.
-__global__ __launch_bounds__(256) void splitk_reduce_bf16(const float* __restrict__ part, uint16_t* __restrict__ Y,
-                                                          int64_t MN, int ks) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= MN) return;
-    float s = 0.f;
-    for (int z = 0; z < ks; ++z) s += part[(int64_t)z * MN + i];
-    Y[i] = f32_to_bf16(s);
+// grid (n_nt, 4 * n_mt): block (nt, 4 mt + rb) finishes row block rb (16
+// rows) of tile (mt, nt); wave w takes its 16 columns n0 + 16 w. The block's
+// h rows (split planes added in split order) are gathered into LDS first;
+// then each lane adds, in fp32, scale_s * h[p] . B_s[n] for its own rows, so
+// every global load of the epilogue is issued before any is waited on.
+// Dynamic LDS: 16 * r_max floats.
+__global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* __restrict__ part_y, int ks, int n_mt,
+                                                                   int n_nt, uint16_t* __restrict__ Y, int M, int N,
+                                                                   Fuse f) {
+    __shared__ SlotMeta meta;
+    extern __shared__ float hs[];  // [16][r_max]
+    const int nt = blockIdx.x, mt = blockIdx.y >> 2, rb = blockIdx.y & 3;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int p0 = mt * 64 + rb * 16;
+    if (p0 >= M) return;  // uniform for the block
+    const f32x4* in = reinterpret_cast<const f32x4*>(part_y);
+    const int64_t zstride = (int64_t)n_mt * n_nt * 16 * 64;
+    const int64_t o = (((int64_t)mt * n_nt + nt) * 16 + rb * 4 + w) * 64 + lane;
+    // splits are added in split order; loads are issued unconditionally from
+    // clamped addresses (a load under a branch is waited on inside it) and
+    // the extra ones are not added
+    f32x4 part[8];
+#pragma unroll
+    for (int z = 0; z < 8; ++z) part[z] = in[min(z, ks - 1) * zstride + o];
+    const MetaView mv = stage_meta(f, &meta);
+    if (f.adapters) {
+        const int nh = 16 * f.r_max;
+        for (int i = threadIdx.x; i < nh; i += kThreads) {
+            const int p = p0 + i / f.r_max;
+            const float* hp = f.h + (int64_t)min(p, M - 1) * f.r_max + i % f.r_max;
+            float hv[8];
+#pragma unroll
+            for (int z = 0; z < 8; ++z) hv[z] = hp[min(z, f.h_splits - 1) * f.h_plane];
+            float v = 0.f;
+#pragma unroll
+            for (int z = 0; z < 8; ++z)
+                if (z < f.h_splits) v += hv[z];
+            for (int z0 = 8; z0 < f.h_splits; z0 += 8) {
+#pragma unroll
+                for (int z = 0; z < 8; ++z) hv[z] = hp[min(z0 + z, f.h_splits - 1) * f.h_plane];
+#pragma unroll
+                for (int z = 0; z < 8; ++z)
+                    if (z0 + z < f.h_splits) v += hv[z];
+            }
+            hs[i] = p < M ? v : 0.f;
+        }
+    }
+    __syncthreads();
+    f32x4 acc = part[0];
+#pragma unroll
+    for (int z = 1; z < 8; ++z)
+        if (z < ks) acc += part[z];
+    for (int z0 = 8; z0 < ks; z0 += 8) {
+#pragma unroll
+        for (int z = 0; z < 8; ++z) part[z] = in[min(z0 + z, ks - 1) * zstride + o];
+#pragma unroll
+        for (int z = 0; z < 8; ++z)
+            if (z0 + z < ks) acc += part[z];
+    }
+    const int n = nt * 64 + w * 16 + (lane & 15);
+    if (f.adapters && n < N) {
+        // lane rows p0 + 4 (lane / 16) + e; rows past M and on slot 0 / rank 0 add nothing
+        int rr[4];
+        const uint16_t* bp[4];
+        float sc[4];
+        int rmax = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int p = p0 + (lane >> 4) * 4 + e;
+            const int s = p < M ? slot_of(mv.indptr, f.S, p) : 0;
+            rr[e] = s == 0 ? 0 : mv.rank[s];
+            sc[e] = mv.scale[s];
+            bp[e] = f.B_pool + ((int64_t)s * N + n) * f.r_max;
+            rmax = max(rmax, rr[e]);
+        }
+        float d[4] = {0.f, 0.f, 0.f, 0.f};
+        if ((f.r_max & 7) == 0) {
+            for (int q0 = 0; q0 < rmax; q0 += 16) {  // 16 ranks of every row per round of loads
+                u32x4 b[4][2];  // B rows are zero past r; chunks past r read zeros
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) b[e][c] = *or_zero(q0 + 8 * c < rr[e], bp[e] + q0 + 8 * c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float* hr = hs + ((lane >> 4) * 4 + e) * f.r_max + q0;
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int q = q0 + 8 * c + 2 * t;
+                            const uint32_t wv = b[e][c][t];
+                            if (q < rr[e]) d[e] = __builtin_fmaf(hr[8 * c + 2 * t], __uint_as_float(wv << 16), d[e]);
+                            if (q + 1 < rr[e])
+                                d[e] = __builtin_fmaf(hr[8 * c + 2 * t + 1], __uint_as_float(wv & 0xffff0000u), d[e]);
+                        }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float* hr = hs + ((lane >> 4) * 4 + e) * f.r_max;
+                for (int q = 0; q < rr[e]; ++q) d[e] = __builtin_fmaf(hr[q], bf16_to_f32(bp[e][q]), d[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (rr[e] > 0) acc[e] = __builtin_fmaf(sc[e], d[e], acc[e]);
+    }
+    f32x4 out[1][1] = {{acc}};
+    store_tile<1, 1>(out, Y, f.token_order, p0, nt * 64 + w * 16, M, N, lane);
 }
 
+// ------------------------------------------------------------------ plan --
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-GemmShape gemm_bf16_shape(int M, int N, int K) {
-    GemmShape g{256, 256, 1, 0};
-    const int kt = cdiv(K, kBK);
-    if ((int64_t)cdiv(M, 256) * cdiv(N, 256) >= 256) {
-        g = {256, 256, 1, kt * kBK};
-    } else if ((int64_t)cdiv(M, 128) * cdiv(N, 128) >= 256) {
-        g = {128, 128, 1, kt * kBK};
-    } else {
-        const int bm = M > 64 ? 128 : 64;
-        const int bn = bm;
-        const int tiles = cdiv(M, bm) * cdiv(N, bn);
-        int ks = 256 / (tiles > 0 ? tiles : 1);
-        ks = ks < 1 ? 1 : ks;
-        const int max_ks = kt / 8 > 0 ? kt / 8 : 1;  // at least 512 K per split
-        ks = ks > max_ks ? max_ks : ks;
-        const int chunk_t = cdiv(kt, ks);
-        ks = cdiv(kt, chunk_t);
-        g = {bm, bn, ks, chunk_t * kBK};
-    }
+GemmPlan gemm_bf16_plan(int M, int N, int K) {
+    GemmPlan g{};
+    if (M <= 0 || N <= 0 || K <= 0) return g;  // nothing to launch
+    const int64_t t256 = (int64_t)cdiv(M, 256) * cdiv(N, 256);
+    const int64_t t128 = (int64_t)cdiv(M, 128) * cdiv(N, 128);
+    const int64_t t64 = (int64_t)cdiv(M, 64) * cdiv(N, 128);
+    if (t256 >= 256) { g.bm = 256; g.bn = 256; return g; }
+    if (t128 >= 256) { g.bm = 128; g.bn = 128; return g; }
+    if (M > 256 && t64 >= 128) { g.bm = 64; g.bn = 128; return g; }
+    // split-K: 64 x 64 tiles, enough K splits for ~256 workgroups
+    g.bm = 64; g.bn = 64;
+    g.n_mt = cdiv(M, 64);
+    g.n_nt = cdiv(N, 64);
+    const int tiles = g.n_mt * g.n_nt;
+    const int want = tiles >= 256 ? 1 : cdiv(256, tiles);
+    const int need = cdiv(cdiv(K, want), 128);  // sub-chunks per split
+    int nsub = 1;
+    while (nsub < need && nsub < 16) nsub *= 2;
+    g.nsub = nsub;
+    g.ks = cdiv(K, nsub * 128);
     return g;
 }
 
-size_t gemm_bf16_workspace(int M, int N, int K) {
-    GemmShape g = gemm_bf16_shape(M, N, K);
-    return g.ks > 1 ? (size_t)g.ks * M * N * sizeof(float) : 0;
+size_t gemm_bf16_workspace(int M, int N, int K, int r_max) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    const GemmPlan g = gemm_bf16_plan(M, N, K);
+    // fp32 h [M][r_max], or bf16 hi / lo [M][2][round_up(r_max, 8)]
+    const size_t h_final = (size_t)M * ((r_max + 7) & ~7) * sizeof(float);
+    if (g.nsub == 0) return (h_final + 255) & ~size_t(255);
+    const size_t py = (size_t)g.ks * g.n_mt * g.n_nt * 16 * 64 * 16;
+    const size_t ph = (size_t)g.ks * M * r_max * sizeof(float);
+    return ((py + 255) & ~size_t(255)) + ((ph + 255) & ~size_t(255));
 }
 
 template <int BM, int BN>
-static hipError_t launch(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, float* ws,
-                         const GemmShape& g, hipStream_t st, StageTimer* tm) {
+static hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K,
+                               const Fuse& f, hipStream_t st, StageTimer* tm) {
     const int tiles_m = cdiv(M, BM), tiles_n = cdiv(N, BN);
-    dim3 grid(tiles_m * tiles_n, g.ks);
-    if (g.ks > 1) {
-        {
-            TimedScope ts(tm, "gemm_bf16", st);
-            gemm_bf16_kernel<BM, BN, true>
-                <<<grid, kThreads, 0, st>>>(X, W, ws, M, N, K, g.k_chunk, tiles_m, tiles_n);
-        }
-        const int64_t MN = (int64_t)M * N;
-        TimedScope ts(tm, "gemm_splitk_reduce", st);
-        splitk_reduce_bf16<<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(ws, Y, MN, g.ks);
-    } else {
-        TimedScope ts(tm, "gemm_bf16", st);
-        gemm_bf16_kernel<BM, BN, false><<<grid, kThreads, 0, st>>>(X, W, Y, M, N, K, g.k_chunk, tiles_m, tiles_n);
-    }
-    return hipGetLastError();
+    return launch(tm, "gemm_bf16", gemm_tiled_kernel<BM, BN>, dim3(tiles_m * tiles_n), dim3(kThreads), st, X, W, Y,
+                  M, N, K, tiles_m, tiles_n, f);
 }
 
-hipError_t gemm_bf16(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, float* ws,
-                     hipStream_t st, StageTimer* tm) {
+template <int NSUB>
+static hipError_t launch_split(const SplitArgs& a, int n_blocks, hipStream_t st, StageTimer* tm) {
+    return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB>, dim3(n_blocks), dim3(kThreads), st, a);
+}
+
+hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {
+    const int M = L.M, N = L.N, K = L.K;
     if (M == 0 || N == 0) return hipSuccess;
-    const GemmShape g = gemm_bf16_shape(M, N, K);
-    if (g.bm == 256) return launch<256, 256>(X, W, Y, M, N, K, ws, g, st, tm);
-    if (g.bm == 128) return launch<128, 128>(X, W, Y, M, N, K, ws, g, st, tm);
-    return launch<64, 64>(X, W, Y, M, N, K, ws, g, st, tm);
+    const GemmPlan g = gemm_bf16_plan(M, N, K);
+    Fuse f{L.token_order, L.slot_indptr, nullptr, L.B_pool, L.rank, L.scale, L.S, L.r_max, 1, 0, L.adapters,
+           nullptr, (L.r_max + 7) & ~7};
+    char* ws = static_cast<char*>(L.workspace);
+    if (g.nsub == 0) {
+        // shrink to final h, then the tiled GEMM with the expand in its epilogue
+        // r_max % 8 == 0: the expand runs as extra K steps (operand: scaled
+        // h as bf16 hi / lo); otherwise in the epilogue from fp32 h
+        float* hbuf = reinterpret_cast<float*>(ws);
+        uint16_t* ext = (L.r_max % 8 == 0) ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+        f.h = ext ? nullptr : hbuf;
+        f.ext = ext;
+        if (L.adapters) {
+            const hipError_t e = sgmv_shrink(1, L.X, L.A_pool, L.rank, L.token_order, L.work, L.n_items,
+                                             ext ? nullptr : hbuf, K, L.r_max, st, tm, L.scale, ext);
+            if (e != hipSuccess) return e;
+        }
+        if (g.bm == 256) return launch_tiled<256, 256>(L.X, L.W, L.Y, M, N, K, f, st, tm);
+        if (g.bm == 128) return launch_tiled<128, 128>(L.X, L.W, L.Y, M, N, K, f, st, tm);
+        return launch_tiled<64, 128>(L.X, L.W, L.Y, M, N, K, f, st, tm);
+    }
+    const size_t py = ((size_t)g.ks * g.n_mt * g.n_nt * 16 * 64 * 16 + 255) & ~size_t(255);
+    SplitArgs a{L.X, L.W, reinterpret_cast<float*>(ws), M, N, K, g.n_mt, g.n_nt, g.ks,
+                L.A_pool, L.rank, L.token_order, reinterpret_cast<const Item*>(L.work),
+                L.adapters ? L.n_items : 0, L.r_max, reinterpret_cast<float*>(ws + py)};
+    const int n_blocks = a.n_items * g.ks + g.n_mt * g.n_nt * g.ks;
+    hipError_t e;
+    switch (g.nsub) {
+        case 1: e = launch_split<1>(a, n_blocks, st, tm); break;
+        case 2: e = launch_split<2>(a, n_blocks, st, tm); break;
+        case 4: e = launch_split<4>(a, n_blocks, st, tm); break;
+        case 8: e = launch_split<8>(a, n_blocks, st, tm); break;
+        default: e = launch_split<16>(a, n_blocks, st, tm); break;
+    }
+    if (e != hipSuccess) return e;
+    f.h = a.part_h;
+    f.h_splits = g.ks;
+    f.h_plane = (int64_t)M * L.r_max;
+    return launch_shm(tm, "gemm_splitk_epilogue", splitk_epilogue_kernel, dim3(g.n_nt, 4 * g.n_mt), dim3(kThreads),
+                      L.adapters ? (uint32_t)(16 * L.r_max * sizeof(float)) : 0u, st,
+                  (const float*)a.part_y, g.ks, g.n_mt, g.n_nt, L.Y, M, N, f);
 }
 
 }  // namespace lora

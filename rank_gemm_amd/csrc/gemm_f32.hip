@@ -47,10 +47,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 hipError_t gemm_f32(const float* X, const float* W, float* Y, int M, int N, int K, hipStream_t st, StageTimer* tm) {
     if (M == 0 || N == 0) return hipSuccess;
-    dim3 grid((N + 63) / 64, (M + 63) / 64);
-    TimedScope ts(tm, "gemm_f32", st);
-    gemm_f32_kernel<<<grid, 256, 0, st>>>(X, W, Y, M, N, K);
-    return hipGetLastError();
+    return launch(tm, "gemm_f32", gemm_f32_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), st, X, W, Y, M, N,
+                  K);
 }
 
 }  // namespace lora

@@ -1,56 +1,82 @@
 // Host-side launchers of the liblora gfx950 kernels (internal interface).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace lora {
 
-// Optional per-kernel timing: when a timer is passed, each launcher records a
-// HIP event pair around every kernel it launches, on the launch stream.
+// Optional per-kernel timing. When a timer is given, a kernel is launched with
+// hipExtLaunchKernel and a pair of events that the runtime stamps with the
+// kernel's own start and end on its stream (no marker packets around it).
 struct StageTimer {
-    virtual void begin(const char* kernel, hipStream_t st) = 0;
-    virtual void end(hipStream_t st) = 0;
+    // events to attach to the next launch of `kernel`; false: launch untimed
+    virtual bool pair(const char* kernel, hipEvent_t* start, hipEvent_t* stop) = 0;
     virtual ~StageTimer() = default;
 };
 
-struct TimedScope {
-    StageTimer* t;
-    hipStream_t st;
-    TimedScope(StageTimer* t_, const char* name, hipStream_t s) : t(t_), st(s) {
-        if (t) t->begin(name, st);
-    }
-    ~TimedScope() {
-        if (t) t->end(st);
-    }
-};
+template <typename... Params, typename... Args>
+inline hipError_t launch_shm(StageTimer* tm, const char* name, void (*kernel)(Params...), dim3 grid, dim3 block,
+                             uint32_t shmem, hipStream_t st, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (tm && tm->pair(name, &e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0, static_cast<Params>(args)...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, st, static_cast<Params>(args)...);
+    return hipGetLastError();
+}
 
-// ---- base GEMM: Y[M][N] = X[M][K] * W[N][K]^T --------------------------
-struct GemmShape {
-    int bm, bn;   // macro tile
-    int ks;       // K splits (1 = no split, result written directly)
-    int k_chunk;  // K elements per split (multiple of 64)
+template <typename... Params, typename... Args>
+inline hipError_t launch(StageTimer* tm, const char* name, void (*kernel)(Params...), dim3 grid, dim3 block,
+                         hipStream_t st, Args... args) {
+    return launch_shm(tm, name, kernel, grid, block, 0, st, args...);
+}
+
+// ---- bf16 forward: shrink + base GEMM with the expand in its epilogue ------
+// y[token_order[p]] = bf16(x[token_order[p]] W^T + scale_s h[p] B_s^T), rows
+// visited in plan order; with adapters == 0 the correction is skipped.
+struct GemmPlan {
+    int bm, bn;          // macro tile of the tiled path
+    int nsub;            // split-K path: 128-wide K sub-chunks per split (0 = tiled path)
+    int ks, n_mt, n_nt;  // split-K path: splits and 64 x 64 tile grid
 };
-GemmShape gemm_bf16_shape(int M, int N, int K);
-size_t gemm_bf16_workspace(int M, int N, int K);  // fp32 split-K partials
-hipError_t gemm_bf16(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, float* ws,
-                     hipStream_t st, StageTimer* tm);
+GemmPlan gemm_bf16_plan(int M, int N, int K);
+size_t gemm_bf16_workspace(int M, int N, int K, int r_max);
+
+struct LinearArgs {
+    const uint16_t* X;
+    const uint16_t* W;
+    uint16_t* Y;
+    int M, N, K;
+    const int32_t* token_order;
+    const int32_t* slot_indptr;
+    const int32_t* work;
+    int n_items;
+    const uint16_t* A_pool;
+    const uint16_t* B_pool;
+    const int32_t* rank;
+    const float* scale;
+    int S, r_max;
+    int adapters;
+    void* workspace;
+};
+hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm);
 hipError_t gemm_f32(const float* X, const float* W, float* Y, int M, int N, int K, hipStream_t st, StageTimer* tm);
 
-// ---- SGMV shrink / expand ------------------------------------------------
-// Shrink partials: part[ks][T][r_max] fp32, indexed by sorted position.
-int shrink_splits(int n_items, int K);
-constexpr int kMaxShrinkSplits = 32;
+// ---- SGMV shrink and the fp32 expand -----------------------------------------
+// h: fp32 [T][r_max] indexed by sorted position (rows of adapter items only).
+// With ext (bf16 pools only), writes the expand operand of the tiled GEMM's
+// extra K steps, scale_s * h as bf16 hi / lo: [T][2][round_up(r_max, 8)].
 hipError_t sgmv_shrink(int dtype, const void* X, const void* A_pool, const int32_t* rank,
-                       const int32_t* token_order, const int32_t* work, int n_items, float* part, int ks, int T,
-                       int K, int r_max, hipStream_t st, StageTimer* tm);
-hipError_t sgmv_expand(int dtype, const float* part, int ks, const void* B_pool, const int32_t* rank,
-                       const float* scale, const int32_t* token_order, const int32_t* work, int n_items, void* Y,
-                       int T, int N, int r_max, hipStream_t st, StageTimer* tm);
-hipError_t shrink_to_h(const float* part, int ks, const int32_t* rank, const int32_t* token_order,
-                       const int32_t* slot_indptr, int S, float* h, int T, int r_max, hipStream_t st,
-                       StageTimer* tm);
+                       const int32_t* token_order, const int32_t* work, int n_items, float* h, int K, int r_max,
+                       hipStream_t st, StageTimer* tm, const float* scale = nullptr, uint16_t* ext = nullptr);
+hipError_t sgmv_expand_f32(const float* h, const float* B_pool, const int32_t* rank, const float* scale,
+                           const int32_t* token_order, const int32_t* work, int n_items, float* Y, int N, int r_max,
+                           hipStream_t st, StageTimer* tm);
+hipError_t scatter_h(const float* h, const int32_t* rank, const int32_t* token_order, const int32_t* slot_indptr,
+                     int S, float* h_out, int T, int r_max, hipStream_t st, StageTimer* tm);
 
 // ---- slot pool ------------------------------------------------------------
 hipError_t pool_check_finite(int dtype, const void* p, int64_t n, int* flag, hipStream_t st);

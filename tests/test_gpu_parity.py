@@ -156,6 +156,12 @@ EDGE = [
     (1000, 1024, 520, 9, [0, 16, 16, 8, 16, 16, 16, 16, 16], 16, "bf16"),  # long segments
     (37, 264, 100, 5, [0, 3, 0, 7, 1], 8, "f32"),
     (130, 96, 77, 3, [0, 5, 2], 5, "f32"),
+    (32, 40960, 64, 3, [0, 8, 4], 8, "bf16"),            # split-K path with more than 16 splits
+    (100, 4104, 200, 4, [0, 16, 3, 8], 16, "bf16"),      # split-K: ragged K, T not a multiple of 64
+    (64, 4096, 14336, 5, [0, 16, 16, 16, 16], 16, "bf16"),  # decode-sized T, gate/up width
+    (2048, 256, 2048, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # tiled path, expand as extra K steps, 2 rank chunks
+    (2048, 256, 2048, 4, [0, 3, 5, 2], 5, "bf16"),          # tiled path, r_max % 8 != 0: epilogue expand
+    (4096, 128, 4096, 5, [0, 16, 8, 16, 4], 16, "bf16"),    # 256 x 256 tiles, long segments
 ]
 
 
@@ -166,6 +172,8 @@ def test_edge_shapes(case):
     ids = g.integers(0, S, size=T).astype(np.int32)
     if case == 5:  # long runs: a few big segments and a block of base rows
         ids = np.repeat(g.integers(0, S, size=8), 125).astype(np.int32)
+    if case == 13:  # 16 sequences of 256 tokens, each on one slot
+        ids = np.repeat(g.integers(0, S, size=16), 256).astype(np.int32)
     alphas = [2.0 * r for r in ranks]
     w = make_custom(200 + case, T, d_in, d_out, S, ranks, alphas, ids, dtype=dtype, r_max=r_max)
     proj = w.projections[0]
