@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 5 plain 256 MiB device copies (reference for the FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -68,6 +70,23 @@ def stage_bytes(ids, ranks, d_in, d_out, r_max, es=2):
     base = acc.base_bytes(len(ids), d_in, d_out, es)
     fused = base + sum(es * int(ranks[s]) * d_out for s in seg) + 4 * T_a * r_max
     return {"base": base, "shrink": shrink, "expand": expand, "fused": fused}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None when
+    the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_decode_q_proj.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    src = b"".join(open(os.path.join(ROOT, "rank_gemm_amd", "csrc", n), "rb").read()
+                   for n in ("gemm_bf16.hip", "shrink.h", "common.h", "kernels.h"))
+    if t.get("kernel") != kernel or hashlib.sha256(src).hexdigest() != t.get("sources_sha256"):
+        return None
+    return int(t["bytes_per_launch"])
 
 
 def us_of(stats, name):
@@ -196,7 +215,7 @@ def main():
     k1_bytes = 2 * T * d_in + 2 * d_in * d_out + a_bytes
     k1_gbs = k1_bytes / (t1 * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("splitk_gemm_kernel<8>"),
             "kernel": "splitk_gemm_kernel (base GEMM K-split partials + SGMV shrink workgroups)",
             "bytes_per_launch": k1_bytes, "mean_us": round(t1, 3)}
     call_bytes = sb["base"] + sb["shrink"] + sb["expand"]
@@ -258,6 +277,14 @@ def main():
                    "call_ms": round(call_ms, 4), "tokens_per_s": round(w3.T / (call_ms * 1e-3), 1),
                    "kernels": {k: round(v["mean_ms"] * 1e3, 2) for k, v in s3.items()}}
         log(f"prefill: {prefill}")
+
+    if args.copy_calibration:
+        src = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 x 256 MiB device copies")
 
     # ---- CPU oracle baseline (bounded sample of the same workload) ----------------
     cpu = None
