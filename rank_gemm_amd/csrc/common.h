@@ -12,13 +12,32 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace lora {
 
+// Global-memory pointer. Loads through it are global loads; a generic
+// pointer the compiler cannot place (one picked by a select, or read from a
+// struct) gives flat loads, which also count against the LDS wait counter.
+template <class T>
+using gptr = const __attribute__((address_space(1))) T*;
+
+template <class T>
+__device__ __forceinline__ gptr<T> as_global(const void* p) {
+    return (gptr<T>)p;
+}
+
 // 16 zero bytes in device memory: a masked-off 16-byte load reads from here
 // (the address is selected, not the loaded value, so no load is waited on
 // early and no branch is needed).
 static __device__ const u32x4 kZeros16[1] = {{0, 0, 0, 0}};
 
-__device__ __forceinline__ const u32x4* or_zero(bool ok, const void* p) {
-    return ok ? static_cast<const u32x4*>(p) : kZeros16;
+__device__ __forceinline__ gptr<u32x4> or_zero(bool ok, const void* p) {
+    return ok ? as_global<u32x4>(p) : as_global<u32x4>(kZeros16);
+}
+
+// Keeps the loads issued above this point above it: neither the optimiser
+// nor the instruction scheduler moves memory operations across it, and it
+// does not wait for them (it uses no loaded value).
+__device__ __forceinline__ void issue_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // bf16 bit pattern -> float (exact)

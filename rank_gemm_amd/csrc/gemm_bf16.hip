@@ -361,7 +361,9 @@ struct SplitArgs {
 
 // grid: n_items * ks shrink blocks, then n_mt * n_nt * ks GEMM blocks.
 // Wave w of a GEMM block owns columns n0 + 16 w .. + 15 of a 64 x 64 tile.
-template <int NSUB>
+// EDGE: some tile reaches past M, N or K (masked loads); otherwise every load
+// is unmasked.
+template <int NSUB, bool EDGE>
 __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
     __shared__ u32x4 lds[2 * 64 * 16];  // two 64 x 128 bf16 stages of x (32 KB)
     constexpr int KC = NSUB * 128;
@@ -388,9 +390,8 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
     const int K = a.K;
 
     // interior tiles (every row, column and k of the split inside the
-    // matrices: the uniform common case) load without masks; edge tiles mask
-    // out-of-range elements to zero
-    const bool interior = m0 + 64 <= a.M && nt * 64 + 64 <= a.N && kbeg + KC <= K;
+    // matrices) load without masks; edge tiles mask out-of-range elements
+    const bool interior = !EDGE || (m0 + 64 <= a.M && nt * 64 + 64 <= a.N && kbeg + KC <= K);
     const bool wok = n < a.N;
     const uint16_t* wrow = a.W + (int64_t)min(n, a.N - 1) * K;
     // x staging: 16 threads per row (256 B), 16 rows per pass, 4 passes
@@ -462,53 +463,201 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
 }
 
 // grid (n_nt, 4 * n_mt): block (nt, 4 mt + rb) finishes row block rb (16
-// rows) of tile (mt, nt); wave w takes its 16 columns n0 + 16 w. The block's
-// h rows (split planes added in split order) are gathered into LDS first;
-// then each lane adds, in fp32, scale_s * h[p] . B_s[n] for its own rows, so
-// every global load of the epilogue is issued before any is waited on.
-// Dynamic LDS: 16 * r_max floats.
+// rows) of tile (mt, nt); wave w takes its 16 columns n0 + 16 w. Lane l holds
+// rows p0 + 4 (l / 16) + e, e < 4, of column n0 + 16 w + l % 16.
+//
+// Two rounds of global loads. Round 1: the split partials, the output rows'
+// token indices, the slot metadata (lane s keeps segment start, rank and scale
+// of slot s when S <= 64) and the block's h rows (split planes, added in
+// split order, then kept in LDS). Round 2, addressed by the rows' slots: each
+// lane's B_s rows. Then every lane adds, in fp32, scale_s * h[p] . B_s[n]
+// to its rows, and the tile is rounded once.
+//
+// ADAPT false: no adapter row in the batch (partials only). VEC: r_max % 8
+// == 0 (16-byte h and B loads); otherwise element loads, waited in turn.
+// LANE_META: S <= 64, metadata held one slot per lane; otherwise staged in
+// LDS (one more round). Dynamic LDS: 16 * r_max + 32 floats (the tail keeps
+// the last row's 32-rank reads in bounds; what they read there is not used).
+constexpr int kLaneMetaSlots = 64;
+
+template <bool ADAPT, bool VEC, bool LANE_META>
 __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* __restrict__ part_y, int ks, int n_mt,
                                                                    int n_nt, uint16_t* __restrict__ Y, int M, int N,
                                                                    Fuse f) {
-    __shared__ SlotMeta meta;
-    extern __shared__ float hs[];  // [16][r_max]
     const int nt = blockIdx.x, mt = blockIdx.y >> 2, rb = blockIdx.y & 3;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int p0 = mt * 64 + rb * 16;
     if (p0 >= M) return;  // uniform for the block
     const f32x4* in = reinterpret_cast<const f32x4*>(part_y);
     const int64_t zstride = (int64_t)n_mt * n_nt * 16 * 64;
     const int64_t o = (((int64_t)mt * n_nt + nt) * 16 + rb * 4 + w) * 64 + lane;
+    const int n = nt * 64 + w * 16 + (lane & 15);
     // splits are added in split order; loads are issued unconditionally from
     // clamped addresses (a load under a branch is waited on inside it) and
     // the extra ones are not added
     f32x4 part[8];
 #pragma unroll
     for (int z = 0; z < 8; ++z) part[z] = in[min(z, ks - 1) * zstride + o];
-    const MetaView mv = stage_meta(f, &meta);
-    if (f.adapters) {
-        const int nh = 16 * f.r_max;
-        for (int i = threadIdx.x; i < nh; i += kThreads) {
-            const int p = p0 + i / f.r_max;
-            const float* hp = f.h + (int64_t)min(p, M - 1) * f.r_max + i % f.r_max;
-            float hv[8];
+    int tok[4];
 #pragma unroll
-            for (int z = 0; z < 8; ++z) hv[z] = hp[min(z, f.h_splits - 1) * f.h_plane];
-            float v = 0.f;
+    for (int e = 0; e < 4; ++e) tok[e] = f.token_order[min(p0 + (lane >> 4) * 4 + e, M - 1)];
+
+    float d[4] = {0.f, 0.f, 0.f, 0.f};
+    int rr[4] = {0, 0, 0, 0};
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (ADAPT) {
+        __shared__ SlotMeta meta;
+        extern __shared__ __align__(16) float hs[];  // [16][r_max]
+        const int S = f.S, r_max = f.r_max;
+        int ip = 0, rk = 0;
+        float sv = 0.f;
+        if constexpr (LANE_META) {
+            ip = f.slot_indptr[min(lane, S)];
+            rk = f.rank[min(lane, S - 1)];
+            sv = f.scale[min(lane, S - 1)];
+        }
+        // h: 16 rows x r_max, h_splits planes; 16-byte pieces when VEC
+        constexpr int HU = 2;  // pieces per thread in round 1
+        const int rq = VEC ? r_max >> 2 : r_max;
+        const int npc = 16 * rq;
+        f32x4 hv[HU][8];
+        if constexpr (VEC) {
 #pragma unroll
-            for (int z = 0; z < 8; ++z)
-                if (z < f.h_splits) v += hv[z];
-            for (int z0 = 8; z0 < f.h_splits; z0 += 8) {
-#pragma unroll
-                for (int z = 0; z < 8; ++z) hv[z] = hp[min(z0 + z, f.h_splits - 1) * f.h_plane];
+            for (int u = 0; u < HU; ++u) {
+                const int i = tid + u * kThreads;
+                const int row = i / rq, c = i - row * rq;
+                const float* hp = f.h + (int64_t)min(p0 + row, M - 1) * r_max + c * 4;
 #pragma unroll
                 for (int z = 0; z < 8; ++z)
-                    if (z0 + z < f.h_splits) v += hv[z];
+                    hv[u][z] = __builtin_bit_cast(f32x4, *or_zero(i < npc && z < f.h_splits, hp + (int64_t)z * f.h_plane));
             }
-            hs[i] = p < M ? v : 0.f;
+        }
+        issue_fence();  // round 1 is in flight
+        if constexpr (!LANE_META) {  // large pools: metadata staged in LDS
+            for (int i = tid; i <= S; i += kThreads) {
+                meta.indptr[i] = f.slot_indptr[i];
+                if (i < S) {
+                    meta.rank[i] = f.rank[i];
+                    meta.scale[i] = f.scale[i];
+                }
+            }
+            __syncthreads();
+        }
+        // slots of this lane's rows
+        int sl[4] = {0, 0, 0, 0};
+        if constexpr (LANE_META) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                // slot of row p = number of slots s in 1..S-1 starting at or before p
+                const uint64_t m = __ballot(lane >= 1 && lane < S && ip <= p0 + j);
+                const int sj = p0 + j < M ? __popcll(m) : 0;
+                if ((lane >> 4) == (j >> 2)) sl[j & 3] = sj;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = __shfl(rk, sl[e]);
+                rr[e] = sl[e] == 0 ? 0 : r;
+                sc[e] = __shfl(sv, sl[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = p0 + (lane >> 4) * 4 + e;
+                sl[e] = p < M ? slot_of(meta.indptr, S, p) : 0;
+                rr[e] = sl[e] == 0 ? 0 : meta.rank[sl[e]];
+                sc[e] = meta.scale[sl[e]];
+            }
+        }
+        const uint16_t* bp[4];
+        int rmax = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bp[e] = f.B_pool + ((int64_t)sl[e] * N + min(n, N - 1)) * r_max;
+            rmax = max(rmax, rr[e]);
+        }
+        // round 2 (first 32 ranks), issued before h is written to LDS
+        constexpr int NC = 4;  // 8-rank chunks per row per round
+        u32x4 b[4][NC];
+        auto bload = [&](int q0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) b[e][c] = *or_zero(q0 + 8 * c < rr[e], bp[e] + q0 + 8 * c);
+        };
+        if constexpr (VEC) bload(0);
+        issue_fence();  // round 2 is in flight
+        // h planes added in split order, into LDS
+        if constexpr (VEC) {
+#pragma unroll
+            for (int u = 0; u < HU; ++u) {
+                const int i = tid + u * kThreads;
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int z = 0; z < 8; ++z)
+                    if (z < f.h_splits) v += hv[u][z];
+                for (int z0 = 8; z0 < f.h_splits; z0 += 8) {
+                    const int row = i / rq, c = i - row * rq;
+                    const float* hp = f.h + (int64_t)min(p0 + row, M - 1) * r_max + c * 4;
+#pragma unroll
+                    for (int z = 0; z < 8; ++z)
+                        hv[u][z] = __builtin_bit_cast(
+                            f32x4, *or_zero(i < npc && z0 + z < f.h_splits, hp + (int64_t)(z0 + z) * f.h_plane));
+#pragma unroll
+                    for (int z = 0; z < 8; ++z)
+                        if (z0 + z < f.h_splits) v += hv[u][z];
+                }
+                if (i < npc) reinterpret_cast<f32x4*>(hs)[i] = v;
+            }
+            for (int i = tid + HU * kThreads; i < npc; i += kThreads) {  // r_max > 128
+                const int row = i / rq, c = i - row * rq;
+                const float* hp = f.h + (int64_t)min(p0 + row, M - 1) * r_max + c * 4;
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                for (int z = 0; z < f.h_splits; ++z) v += *as_global<f32x4>(hp + (int64_t)z * f.h_plane);
+                reinterpret_cast<f32x4*>(hs)[i] = v;
+            }
+        } else {
+            for (int i = tid; i < npc; i += kThreads) {
+                const int row = i / r_max;
+                const float* hp = f.h + (int64_t)min(p0 + row, M - 1) * r_max + (i - row * r_max);
+                float v = 0.f;
+                for (int z = 0; z < f.h_splits; ++z) v += hp[(int64_t)z * f.h_plane];
+                hs[i] = v;
+            }
+        }
+        __syncthreads();
+        // fp32 dot products, ranks in order; terms past the row's rank are
+        // computed and dropped by a select (no branch)
+        auto fma_round = [&](int q0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float* hr = hs + ((lane >> 4) * 4 + e) * r_max + q0;
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int q = q0 + 8 * c + 2 * t;
+                        const uint32_t wv = b[e][c][t];
+                        const float t0 = __builtin_fmaf(hr[8 * c + 2 * t], __uint_as_float(wv << 16), d[e]);
+                        d[e] = q < rr[e] ? t0 : d[e];
+                        const float t1 = __builtin_fmaf(hr[8 * c + 2 * t + 1], __uint_as_float(wv & 0xffff0000u), d[e]);
+                        d[e] = q + 1 < rr[e] ? t1 : d[e];
+                    }
+            }
+        };
+        if constexpr (VEC) {
+            fma_round(0);
+            for (int q0 = 8 * NC; q0 < rmax; q0 += 8 * NC) {
+                bload(q0);
+                fma_round(q0);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float* hr = hs + ((lane >> 4) * 4 + e) * r_max;
+                for (int q = 0; q < rr[e]; ++q) d[e] = __builtin_fmaf(hr[q], bf16_to_f32(bp[e][q]), d[e]);
+            }
         }
     }
-    __syncthreads();
     f32x4 acc = part[0];
 #pragma unroll
     for (int z = 1; z < 8; ++z)
@@ -520,58 +669,14 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
         for (int z = 0; z < 8; ++z)
             if (z0 + z < ks) acc += part[z];
     }
-    const int n = nt * 64 + w * 16 + (lane & 15);
-    if (f.adapters && n < N) {
-        // lane rows p0 + 4 (lane / 16) + e; rows past M and on slot 0 / rank 0 add nothing
-        int rr[4];
-        const uint16_t* bp[4];
-        float sc[4];
-        int rmax = 0;
+    if (n >= N) return;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int p = p0 + (lane >> 4) * 4 + e;
-            const int s = p < M ? slot_of(mv.indptr, f.S, p) : 0;
-            rr[e] = s == 0 ? 0 : mv.rank[s];
-            sc[e] = mv.scale[s];
-            bp[e] = f.B_pool + ((int64_t)s * N + n) * f.r_max;
-            rmax = max(rmax, rr[e]);
-        }
-        float d[4] = {0.f, 0.f, 0.f, 0.f};
-        if ((f.r_max & 7) == 0) {
-            for (int q0 = 0; q0 < rmax; q0 += 16) {  // 16 ranks of every row per round of loads
-                u32x4 b[4][2];  // B rows are zero past r; chunks past r read zeros
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) b[e][c] = *or_zero(q0 + 8 * c < rr[e], bp[e] + q0 + 8 * c);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float* hr = hs + ((lane >> 4) * 4 + e) * f.r_max + q0;
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const int q = q0 + 8 * c + 2 * t;
-                            const uint32_t wv = b[e][c][t];
-                            if (q < rr[e]) d[e] = __builtin_fmaf(hr[8 * c + 2 * t], __uint_as_float(wv << 16), d[e]);
-                            if (q + 1 < rr[e])
-                                d[e] = __builtin_fmaf(hr[8 * c + 2 * t + 1], __uint_as_float(wv & 0xffff0000u), d[e]);
-                        }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float* hr = hs + ((lane >> 4) * 4 + e) * f.r_max;
-                for (int q = 0; q < rr[e]; ++q) d[e] = __builtin_fmaf(hr[q], bf16_to_f32(bp[e][q]), d[e]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (rr[e] > 0) acc[e] = __builtin_fmaf(sc[e], d[e], acc[e]);
+    for (int e = 0; e < 4; ++e) {
+        if (p0 + (lane >> 4) * 4 + e >= M) continue;
+        float v = acc[e];
+        if (rr[e] > 0) v = __builtin_fmaf(sc[e], d[e], v);
+        Y[(int64_t)tok[e] * N + n] = f32_to_bf16(v);
     }
-    f32x4 out[1][1] = {{acc}};
-    store_tile<1, 1>(out, Y, f.token_order, p0, nt * 64 + w * 16, M, N, lane);
 }
 
 // ------------------------------------------------------------------ plan --
@@ -621,7 +726,9 @@ static hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y
 
 template <int NSUB>
 static hipError_t launch_split(const SplitArgs& a, int n_blocks, hipStream_t st, StageTimer* tm) {
-    return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB>, dim3(n_blocks), dim3(kThreads), st, a);
+    const bool edge = a.M % 64 != 0 || a.N % 64 != 0 || a.K % (NSUB * 128) != 0;
+    if (edge) return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB, true>, dim3(n_blocks), dim3(kThreads), st, a);
+    return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB, false>, dim3(n_blocks), dim3(kThreads), st, a);
 }
 
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {
@@ -665,9 +772,16 @@ hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm
     f.h = a.part_h;
     f.h_splits = g.ks;
     f.h_plane = (int64_t)M * L.r_max;
-    return launch_shm(tm, "gemm_splitk_epilogue", splitk_epilogue_kernel, dim3(g.n_nt, 4 * g.n_mt), dim3(kThreads),
-                      L.adapters ? (uint32_t)(16 * L.r_max * sizeof(float)) : 0u, st,
-                  (const float*)a.part_y, g.ks, g.n_mt, g.n_nt, L.Y, M, N, f);
+    const dim3 eg(g.n_nt, 4 * g.n_mt);
+    auto epi = splitk_epilogue_kernel<false, false, false>;
+    if (L.adapters) {
+        if (L.r_max % 8 != 0) epi = splitk_epilogue_kernel<true, false, false>;
+        else if (L.S <= kLaneMetaSlots) epi = splitk_epilogue_kernel<true, true, true>;
+        else epi = splitk_epilogue_kernel<true, true, false>;
+    }
+    const uint32_t shm = L.adapters ? (uint32_t)((16 * L.r_max + 32) * sizeof(float)) : 0u;
+    return launch_shm(tm, "gemm_splitk_epilogue", epi, eg, dim3(kThreads), shm, st, (const float*)a.part_y, g.ks,
+                      g.n_mt, g.n_nt, L.Y, M, N, f);
 }
 
 }  // namespace lora
