@@ -27,6 +27,8 @@
 #include "kernels.h"
 #include "shrink.h"
 
+#include <type_traits>
+
 namespace lora {
 
 constexpr int kBK = 64;
@@ -198,21 +200,21 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // 2 rp (rp = r_max rounded up to 8): the A operand of row p is its ext row
 // [bf16 hi of scale_s h | lo remainder] (zero for rows of other segments),
 // the B operand of column n is [B_s[n] | B_s[n]], so the products add
-// scale_s h . B_s. The extension is walked in steps of 64.
+// scale_s h . B_s. The extension is walked in steps of 64 (or 32).
 struct ExtraStep {
     int s, sb, se, r, t;
 };
 
-// Number of extra steps (e < 0) or the decoding of step e.
+// Number of extra steps of `step` k (e < 0) or the decoding of step e.
 __device__ __forceinline__ int extra_steps(const MetaView& mv, const Fuse& f, int m0, int mend, int e,
-                                           ExtraStep* out) {
+                                           ExtraStep* out, int step = 64) {
     int n = 0;
     for (int s = slot_of(mv.indptr, f.S, m0); s < f.S; ++s) {
         const int sb = mv.indptr[s], se = mv.indptr[s + 1];
         if (sb >= mend) break;
         const int r = mv.rank[s];
         if (s == 0 || r == 0 || se <= m0 || se <= sb) continue;
-        const int k = (2 * f.rp + 63) >> 6;
+        const int k = (2 * f.rp + step - 1) / step;
         if (e >= 0 && e < n + k) {
             *out = ExtraStep{s, sb, se, r, e - n};
             return e;
@@ -339,6 +341,187 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const uint16_t*
     const int p0 = m0 + wm * WTM, nb = n0 + wn * WTN;
     if (!f.ext) fused_expand<FM, FN>(acc, f, mv, p0, nb, M, N, lane);
     store_tile<FM, FN>(acc, Y, f.token_order, p0, nb, M, N, lane);
+}
+
+// ------------------------------------------------------- tiled, 256 x 256 --
+// 8 waves (2 per SIMD) as 2 x 4, wave tile 128 x 64 (8 x 4 MFMA tiles); K in
+// stages of 32 through kDmaStages LDS buffers, filled by direct-to-LDS loads
+// (global_load_lds_dwordx4: 16 B per lane, written at the wave's LDS base +
+// 16 * lane). A stage's A and B operands are 16 blocks each of 16 rows x 32 k
+// (1 KB). Lane i of a block load fetches row i / 4, k chunk (i % 4) ^
+// dma_swz(row): the bank swizzle is applied by choosing the source, so the
+// MFMA fragment reads (row l % 16, chunk l / 16) are free of bank conflicts.
+// Stage kt + kDmaStages - 1 is loaded once every wave is past stage kt's
+// barrier. The fragment reads are issued and waited on by hand: with LDS
+// loads in flight the compiler would wait for all of them at the first use.
+constexpr int kDmaStages = 3;
+constexpr int kDmaStageChunks = (256 + 256) * 32 * 2 / 16;  // 16-byte chunks
+
+__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
+
+__device__ __forceinline__ void dma16(gptr<u32x4> src, u32x4* lds_dst) {
+    __builtin_amdgcn_global_load_lds((gptr<void>)src, (lds_void_ptr)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_offset(const u32x4* p) { return (uint32_t)(uintptr_t)(lds_u32x4_ptr)p; }
+
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+    return r;
+}
+// at most N LDS reads of this wave still outstanding; ties the wait to the
+// fragment registers so that no use of them moves above it
+template <int N>
+__device__ __forceinline__ void lds_landed(u32x4& a) {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_landed(u32x4& a, u32x4& b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+// at most N vector-memory ops of this wave outstanding, no LDS op
+template <int N>
+__device__ __forceinline__ void vm_landed() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// EPI: the expand runs in the epilogue from fp32 h (r_max % 8 != 0);
+// otherwise it runs as extra K steps (or there is no adapter row).
+template <bool EPI>
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_dma_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
+    int tiles_m, int tiles_n, Fuse f) {
+    constexpr int BM = 256, BN = 256, BK = 32, NS = kDmaStages, STAGE = kDmaStageChunks;
+    __shared__ u32x4 lds[NS * STAGE];
+    __shared__ SlotMeta meta;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const MetaView mv = stage_meta(f, &meta);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int mend = min(M, m0 + BM);
+    const int nk = (K + BK - 1) / BK;
+    // this lane's rows of the two A and two B blocks it loads (rows past M or
+    // N are clamped: their products land in outputs that are not stored)
+    const int rl = lane >> 2;
+    const int cl = (lane & 3) ^ dma_swz(rl);
+    int prow[2], ncol[2];
+    const uint16_t* ap[2];
+    const uint16_t* bp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        prow[b] = m0 + (wave * 2 + b) * 16 + rl;
+        ncol[b] = n0 + (wave * 2 + b) * 16 + rl;
+        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + cl * 8;
+        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
+    }
+    __syncthreads();  // slot metadata staged
+    const int nt = nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0);
+
+    auto issue = [&](int kt) {
+        u32x4* st = lds + (kt % NS) * STAGE;
+        gptr<u32x4> asrc[2], bsrc[2];
+        if (kt < nk) {
+            const int k = kt * BK;
+            const bool kin = k + cl * 8 < K;  // K % 8 == 0: a chunk is fully in or out
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                asrc[b] = or_zero(kin, ap[b] + k);
+                bsrc[b] = or_zero(kin, bp[b] + k);
+            }
+        } else {
+            ExtraStep x{};
+            extra_steps(mv, f, m0, mend, kt - nk, &x, BK);
+            const int k = x.t * BK + cl * 8;            // position in the 2 rp extension
+            const int q = k < f.rp ? k : k - f.rp;      // rank of the chunk (rp % 8 == 0)
+            const bool qin = k < 2 * f.rp && q < x.r;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                asrc[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
+                bsrc[b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) dma16(asrc[b], st + (wave * 2 + b) * 64);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) dma16(bsrc[b], st + 16 * 64 + (wave * 2 + b) * 64);
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int fr = lane & 15, fc = lane >> 4;
+    const int foff = fr * 4 + (fc ^ dma_swz(fr));
+    const uint32_t abase = lds_offset(lds + wm * 8 * 64 + foff);
+    const uint32_t bbase = lds_offset(lds + 16 * 64 + wn * 4 * 64 + foff);
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nt) issue(s);
+    for (int kt = 0; kt < nt; ++kt) {
+        // stage kt landed for this wave (the one issued after it may be in flight)
+        static_assert(NS == 3, "wait counts assume 3 stages");
+        if (kt + 1 < nt) vm_landed<4>();
+        else vm_landed<0>();
+        stage_barrier();
+        if (kt + NS - 1 < nt) issue(kt + NS - 1);  // into stage kt - 1's buffer
+        const uint32_t so = (kt % NS) * STAGE * 16;
+        u32x4 bf[4], af[8];
+        bf[0] = lds_read16<0>(bbase + so);
+        bf[1] = lds_read16<1024>(bbase + so);
+        bf[2] = lds_read16<2048>(bbase + so);
+        bf[3] = lds_read16<3072>(bbase + so);
+        af[0] = lds_read16<0>(abase + so);
+        af[1] = lds_read16<1024>(abase + so);
+        af[2] = lds_read16<2048>(abase + so);
+        af[3] = lds_read16<3072>(abase + so);
+        af[4] = lds_read16<4096>(abase + so);
+        af[5] = lds_read16<5120>(abase + so);
+        af[6] = lds_read16<6144>(abase + so);
+        af[7] = lds_read16<7168>(abase + so);
+        lds_landed<7>(bf[0], af[0]);
+        lds_landed<7>(bf[1], bf[2]);
+        lds_landed<7>(bf[3]);
+        auto row = [&](auto i_) {
+            constexpr int i = decltype(i_)::value;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        row(std::integral_constant<int, 0>{});
+        lds_landed<6>(af[1]);
+        row(std::integral_constant<int, 1>{});
+        lds_landed<5>(af[2]);
+        row(std::integral_constant<int, 2>{});
+        lds_landed<4>(af[3]);
+        row(std::integral_constant<int, 3>{});
+        lds_landed<3>(af[4]);
+        row(std::integral_constant<int, 4>{});
+        lds_landed<2>(af[5]);
+        row(std::integral_constant<int, 5>{});
+        lds_landed<1>(af[6]);
+        row(std::integral_constant<int, 6>{});
+        lds_landed<0>(af[7]);
+        row(std::integral_constant<int, 7>{});
+    }
+    const int p0 = m0 + wm * 128, nb = n0 + wn * 64;
+    if constexpr (EPI) fused_expand<8, 4>(acc, f, mv, p0, nb, M, N, lane);
+    store_tile<8, 4>(acc, Y, f.token_order, p0, nb, M, N, lane);
 }
 
 // -------------------------------------------------------------- split-K --
@@ -751,7 +934,12 @@ hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm
                                              ext ? nullptr : hbuf, K, L.r_max, st, tm, L.scale, ext);
             if (e != hipSuccess) return e;
         }
-        if (g.bm == 256) return launch_tiled<256, 256>(L.X, L.W, L.Y, M, N, K, f, st, tm);
+        if (g.bm == 256) {
+            const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
+            auto ker = (L.adapters && !f.ext) ? gemm_dma_kernel<true> : gemm_dma_kernel<false>;
+            return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(512), st, L.X, L.W, L.Y, M, N, K, tiles_m,
+                          tiles_n, f);
+        }
         if (g.bm == 128) return launch_tiled<128, 128>(L.X, L.W, L.Y, M, N, K, f, st, tm);
         return launch_tiled<64, 128>(L.X, L.W, L.Y, M, N, K, f, st, tm);
     }

@@ -162,6 +162,8 @@ EDGE = [
     (2048, 256, 2048, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # tiled path, expand as extra K steps, 2 rank chunks
     (2048, 256, 2048, 4, [0, 3, 5, 2], 5, "bf16"),          # tiled path, r_max % 8 != 0: epilogue expand
     (4096, 128, 4096, 5, [0, 16, 8, 16, 4], 16, "bf16"),    # 256 x 256 tiles, long segments
+    (4000, 136, 4100, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # 256 x 256 tiles: ragged T, d_out, d_in; 5 extension steps
+    (3900, 264, 4200, 4, [0, 3, 5, 2], 5, "bf16"),          # 256 x 256 tiles, r_max % 8 != 0: epilogue expand
 ]
 
 
@@ -174,6 +176,8 @@ def test_edge_shapes(case):
         ids = np.repeat(g.integers(0, S, size=8), 125).astype(np.int32)
     if case == 13:  # 16 sequences of 256 tokens, each on one slot
         ids = np.repeat(g.integers(0, S, size=16), 256).astype(np.int32)
+    if case == 14:  # 40 sequences of 100 tokens: segments that cross tile rows
+        ids = np.repeat(g.integers(0, S, size=40), 100).astype(np.int32)
     alphas = [2.0 * r for r in ranks]
     w = make_custom(200 + case, T, d_in, d_out, S, ranks, alphas, ids, dtype=dtype, r_max=r_max)
     proj = w.projections[0]
