@@ -14,15 +14,16 @@
 // equal those of a run with no adapter row.
 //
 // Two paths:
-//  * tiled (prefill-sized T): BM x BN macro tiles, 4 waves in 2 x 2, K in
-//    steps of 64 through a double-buffered, XOR-swizzled LDS stage; the
-//    shrink runs before it as its own kernel.
+//  * tiled (prefill-sized T): 256 x 256 macro tiles over 8 waves with K in
+//    stages of 32 through a 3-deep LDS ring filled by direct-to-LDS loads
+//    (128 x 128 and 64 x 128 tiles with 4 waves and register-staged loads for
+//    smaller T); the shrink runs before it as its own kernel.
 //  * split-K (decode-sized T): kernel 1 computes 64 x 64 output tiles over K
-//    splits, gathering x rows into LDS in 128-wide sub-chunks while W is
-//    streamed from HBM straight into registers two sub-chunks ahead; extra
-//    workgroups of the same launch compute the shrink over the same K
-//    splits. Kernel 2 adds the partial products in split order, applies the
-//    expand and rounds once. No workgroup waits on another.
+//    splits, streaming the split's gathered x rows and W rows through a
+//    5-deep LDS ring of 64-k stages by direct-to-LDS loads; extra workgroups
+//    of the same launch compute the shrink over the same K splits. Kernel 2
+//    adds the partial products in split order, applies the expand and rounds
+//    once. No workgroup waits on another.
 #include "common.h"
 #include "kernels.h"
 #include "shrink.h"
@@ -525,9 +526,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 }
 
 // -------------------------------------------------------------- split-K --
-// LDS chunk (row, c) for sub-chunks of 128 k: 16 chunks per row.
-__device__ __forceinline__ int swz16(int row, int c) { return row * 16 + (c ^ (row & 15)); }
-
 struct SplitArgs {
     const uint16_t* X;
     const uint16_t* W;
@@ -544,12 +542,20 @@ struct SplitArgs {
 
 // grid: n_items * ks shrink blocks, then n_mt * n_nt * ks GEMM blocks.
 // Wave w of a GEMM block owns columns n0 + 16 w .. + 15 of a 64 x 64 tile.
-// EDGE: some tile reaches past M, N or K (masked loads); otherwise every load
-// is unmasked.
-template <int NSUB, bool EDGE>
+// The split's x rows (gathered through token_order) and W rows stream
+// through kSplitStages LDS buffers of 64 k by direct-to-LDS loads: a stage is
+// 8 blocks each of x and of W, a block being 8 rows x 128 B; lane i of a
+// block load fetches row i / 8, chunk (i % 8) ^ (row % 8), so that each load
+// instruction reads whole 128-byte lines and the MFMA fragment reads (row
+// l % 16, chunk l / 16) are free of bank conflicts. Rows past M or N are
+// clamped (their partials are not stored); chunks past K read zeros.
+constexpr int kSplitStages = 5;
+constexpr int kSplitStageChunks = 1024;  // 16-byte chunks: x 512, W 512
+
+template <int NSUB>
 __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
-    __shared__ u32x4 lds[2 * 64 * 16];  // two 64 x 128 bf16 stages of x (32 KB)
-    constexpr int KC = NSUB * 128;
+    __shared__ u32x4 lds[kSplitStages * kSplitStageChunks];  // 80 KB
+    constexpr int KC = NSUB * 128, NST = NSUB * 2, NS = kSplitStages, SC = kSplitStageChunks;
     const int n_shrink = a.n_items * a.ks;
     if ((int)blockIdx.x < n_shrink) {
         const int item = blockIdx.x % a.n_items, kz = blockIdx.x / a.n_items;
@@ -566,79 +572,59 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
     const int tiles = a.n_mt * a.n_nt;
     const int kz = g / tiles, t = g - kz * tiles;
     const int mt = t / a.n_nt, nt = t - mt * a.n_nt;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, kg = lane >> 4;
-    const int m0 = mt * 64, n = nt * 64 + wave * 16 + col;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m0 = mt * 64, n0 = nt * 64;
     const int kbeg = kz * KC;
     const int K = a.K;
-
-    // interior tiles (every row, column and k of the split inside the
-    // matrices) load without masks; edge tiles mask out-of-range elements
-    const bool interior = !EDGE || (m0 + 64 <= a.M && nt * 64 + 64 <= a.N && kbeg + KC <= K);
-    const bool wok = n < a.N;
-    const uint16_t* wrow = a.W + (int64_t)min(n, a.N - 1) * K;
-    // x staging: 16 threads per row (256 B), 16 rows per pass, 4 passes
-    const int xr = tid >> 4, xc = tid & 15;
-    const uint16_t* xrow[4];
-    bool xok[4];
-    u32x4 xreg[4];
-    auto xload = [&](int j) {
-        const int kk = kbeg + j * 128 + xc * 8;
-        if (interior) {
+    // this lane's rows and chunk in its two x and two W block loads
+    const int dr = lane >> 3, dc = lane & 7;
+    const uint16_t* xs[2];
+    const uint16_t* ws[2];
+    int kc[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xreg[i] = *(const u32x4*)(xrow[i] + kk);
-        } else {
+    for (int j = 0; j < 2; ++j) {
+        const int r = 16 * wave + 8 * j + dr;  // tile row / column 0..63
+        kc[j] = kbeg + (dc ^ (r & 7)) * 8;     // this lane's k within a stage
+        xs[j] = a.X + (int64_t)a.token_order[min(m0 + r, a.M - 1)] * K + kc[j];
+        ws[j] = a.W + (int64_t)min(n0 + r, a.N - 1) * K + kc[j];
+    }
+    auto issue = [&](int s) {
+        u32x4* st = lds + (s % NS) * SC;
+        const int k = s * 64;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xreg[i] = *or_zero(xok[i] && kk < K, xrow[i] + kk);
-        }
+        for (int j = 0; j < 2; ++j) dma16(or_zero(kc[j] + k < K, xs[j] + k), st + (2 * wave + j) * 64);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16(or_zero(kc[j] + k < K, ws[j] + k), st + 512 + (2 * wave + j) * 64);
     };
-    auto xstore = [&](int b) {
+    // fragment reads: row r = lane % 16 of a 16-row tile, chunk 4 u + lane / 16
+    const int fr = lane & 15, fq = lane >> 4;
+    int fo[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds[b * 1024 + swz16(xr + 16 * i, xc)] = xreg[i];
-    };
-    u32x4 wreg[3][4];
-    auto wload = [&](int j, int slot) {
-        if (interior) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) wreg[slot][u] = *(const u32x4*)(wrow + kbeg + j * 128 + u * 32 + kg * 8);
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int kk = kbeg + j * 128 + u * 32 + kg * 8;
-                wreg[slot][u] = *or_zero(wok && kk < K, wrow + kk);
-            }
-        }
-    };
+    for (int u = 0; u < 2; ++u) fo[u] = fr * 8 + ((4 * u + fq) ^ (fr & 7));
     f32x4 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // W does not depend on the plan: start streaming it before the gather
-    wload(0, 0);
-    if (NSUB > 1) wload(1, 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = m0 + xr + 16 * i;
-        xok[i] = p < a.M;
-        xrow[i] = a.X + (int64_t)a.token_order[min(p, a.M - 1)] * K;
-    }
-    xload(0);
-    xstore(0);
-    __syncthreads();
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < NST) issue(s);
 #pragma unroll
-    for (int j = 0; j < NSUB; ++j) {
-        if (j + 1 < NSUB) xload(j + 1);
-        if (j + 2 < NSUB) wload(j + 2, (j + 2) % 3);
-        u32x4 xf[4][4];  // all of this sub-chunk's x fragments, read before the products
+    for (int s = 0; s < NST; ++s) {
+        // stage s landed for this wave; the stages issued after it may be in flight
+        const int later = (s + NS - 2 < NST ? NS - 2 : NST - 1 - s);
+        static_assert(kSplitStages == 5, "wait counts assume 5 stages");
+        if (later >= 3) vm_landed<12>();
+        else if (later == 2) vm_landed<8>();
+        else if (later == 1) vm_landed<4>();
+        else vm_landed<0>();
+        stage_barrier();
+        if (s + NS - 1 < NST) issue(s + NS - 1);  // into stage s - 1's buffer
+        const u32x4* st = lds + (s % NS) * SC;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 2; ++u) {
+            const u32x4 wf = st[512 + wave * 128 + fo[u]];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xf[u][i] = lds[(j & 1) * 1024 + swz16(i * 16 + col, u * 4 + kg)];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mfma16x16x32(xf[u][i], wreg[j % 3][u], acc[i]);
-        if (j + 1 < NSUB) xstore((j + 1) & 1);
-        __syncthreads();
+            for (int i = 0; i < 4; ++i) acc[i] = mfma16x16x32(st[i * 128 + fo[u]], wf, acc[i]);
+        }
     }
     f32x4* out = reinterpret_cast<f32x4*>(a.part_y) + ((int64_t)(kz * a.n_mt + mt) * a.n_nt + nt) * 16 * 64;
 #pragma unroll
@@ -909,9 +895,7 @@ static hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y
 
 template <int NSUB>
 static hipError_t launch_split(const SplitArgs& a, int n_blocks, hipStream_t st, StageTimer* tm) {
-    const bool edge = a.M % 64 != 0 || a.N % 64 != 0 || a.K % (NSUB * 128) != 0;
-    if (edge) return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB, true>, dim3(n_blocks), dim3(kThreads), st, a);
-    return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB, false>, dim3(n_blocks), dim3(kThreads), st, a);
+    return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB>, dim3(n_blocks), dim3(kThreads), st, a);
 }
 
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {
