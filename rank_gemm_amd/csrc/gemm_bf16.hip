@@ -531,16 +531,18 @@ struct SplitArgs {
     const uint16_t* W;
     float* part_y;  // [ks][n_mt][n_nt][16 fragments][64 lanes] f32x4
     int M, N, K, n_mt, n_nt, ks;
-    // shrink workgroups (the first n_items * ks blocks)
+    // shrink workgroups (the first n_items * hs blocks), hkc k each
     const uint16_t* A_pool;
     const int32_t* rank;
     const int32_t* token_order;
     const Item* work;
     int n_items, r_max;
-    float* part_h;  // [ks][M][r_max]
+    float* part_h;  // [hs][M][r_max]
+    int hs, hkc;
 };
 
-// grid: n_items * ks shrink blocks, then n_mt * n_nt * ks GEMM blocks.
+// grid: n_items * hs shrink blocks, then n_mt * n_nt * ks GEMM blocks. The
+// shrink splits are finer than the GEMM's, so that they finish early.
 // Wave w of a GEMM block owns columns n0 + 16 w .. + 15 of a 64 x 64 tile.
 // The split's x rows (gathered through token_order) and W rows stream
 // through kSplitStages LDS buffers of 64 k by direct-to-LDS loads: a stage is
@@ -556,13 +558,13 @@ template <int NSUB>
 __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
     __shared__ u32x4 lds[kSplitStages * kSplitStageChunks];  // 80 KB
     constexpr int KC = NSUB * 128, NST = NSUB * 2, NS = kSplitStages, SC = kSplitStageChunks;
-    const int n_shrink = a.n_items * a.ks;
+    const int n_shrink = a.n_items * a.hs;
     if ((int)blockIdx.x < n_shrink) {
         const int item = blockIdx.x % a.n_items, kz = blockIdx.x / a.n_items;
         const Item it = a.work[item];
         const int r = a.rank[it.slot];
         if (r == 0) return;
-        const int kbeg = kz * KC, kend = min(a.K, kbeg + KC);
+        const int kbeg = kz * a.hkc, kend = min(a.K, kbeg + a.hkc);
         const ShrinkOut out{a.part_h + (int64_t)kz * a.M * a.r_max, nullptr, 0, 0.f};
         shrink_item<4>(a.X, a.A_pool, r, a.token_order, it, out, a.K, kbeg, kend, a.r_max,
                        reinterpret_cast<f32x4*>(lds));
@@ -871,6 +873,10 @@ GemmPlan gemm_bf16_plan(int M, int N, int K) {
     while (nsub < need && nsub < 16) nsub *= 2;
     g.nsub = nsub;
     g.ks = cdiv(K, nsub * 128);
+    // shrink splits of at least 256 k, at most 8 of them (kernel 2 adds the
+    // h planes in one round of loads)
+    g.hkc = max(256, (cdiv(K, 8) + 31) / 32 * 32);
+    g.hs = cdiv(K, g.hkc);
     return g;
 }
 
@@ -881,7 +887,7 @@ size_t gemm_bf16_workspace(int M, int N, int K, int r_max) {
     const size_t h_final = (size_t)M * ((r_max + 7) & ~7) * sizeof(float);
     if (g.nsub == 0) return (h_final + 255) & ~size_t(255);
     const size_t py = (size_t)g.ks * g.n_mt * g.n_nt * 16 * 64 * 16;
-    const size_t ph = (size_t)g.ks * M * r_max * sizeof(float);
+    const size_t ph = (size_t)g.hs * M * r_max * sizeof(float);
     return ((py + 255) & ~size_t(255)) + ((ph + 255) & ~size_t(255));
 }
 
@@ -930,8 +936,8 @@ hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm
     const size_t py = ((size_t)g.ks * g.n_mt * g.n_nt * 16 * 64 * 16 + 255) & ~size_t(255);
     SplitArgs a{L.X, L.W, reinterpret_cast<float*>(ws), M, N, K, g.n_mt, g.n_nt, g.ks,
                 L.A_pool, L.rank, L.token_order, reinterpret_cast<const Item*>(L.work),
-                L.adapters ? L.n_items : 0, L.r_max, reinterpret_cast<float*>(ws + py)};
-    const int n_blocks = a.n_items * g.ks + g.n_mt * g.n_nt * g.ks;
+                L.adapters ? L.n_items : 0, L.r_max, reinterpret_cast<float*>(ws + py), g.hs, g.hkc};
+    const int n_blocks = a.n_items * g.hs + g.n_mt * g.n_nt * g.ks;
     hipError_t e;
     switch (g.nsub) {
         case 1: e = launch_split<1>(a, n_blocks, st, tm); break;
@@ -942,7 +948,7 @@ hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm
     }
     if (e != hipSuccess) return e;
     f.h = a.part_h;
-    f.h_splits = g.ks;
+    f.h_splits = g.hs;
     f.h_plane = (int64_t)M * L.r_max;
     const dim3 eg(g.n_nt, 4 * g.n_mt);
     auto epi = splitk_epilogue_kernel<false, false, false>;

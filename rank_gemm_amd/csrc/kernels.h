@@ -41,6 +41,7 @@ struct GemmPlan {
     int bm, bn;          // macro tile of the tiled path
     int nsub;            // split-K path: 128-wide K sub-chunks per split (0 = tiled path)
     int ks, n_mt, n_nt;  // split-K path: splits and 64 x 64 tile grid
+    int hs, hkc;         // split-K path: shrink splits of hkc k each (hkc % 32 == 0)
 };
 GemmPlan gemm_bf16_plan(int M, int N, int K);
 size_t gemm_bf16_workspace(int M, int N, int K, int r_max);
