@@ -399,7 +399,8 @@ __device__ __forceinline__ void stage_barrier() {
 
 // EPI: the expand runs in the epilogue from fp32 h (r_max % 8 != 0);
 // otherwise it runs as extra K steps (or there is no adapter row).
-template <bool EPI>
+// KTAIL: K % 32 != 0, the last base stage masks the chunks past K.
+template <bool EPI, bool KTAIL>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, Fuse f) {
@@ -429,18 +430,21 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
     }
     __syncthreads();  // slot metadata staged
-    const int nt = nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0);
+    // the same for every lane; read from LDS it would be a per-lane value, and
+    // the loop would be compiled as divergent control flow
+    const int nt = __builtin_amdgcn_readfirstlane(
+        nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0));
 
     auto issue = [&](int kt) {
         u32x4* st = lds + (kt % NS) * STAGE;
         gptr<u32x4> asrc[2], bsrc[2];
         if (kt < nk) {
             const int k = kt * BK;
-            const bool kin = k + cl * 8 < K;  // K % 8 == 0: a chunk is fully in or out
+            const bool kin = !KTAIL || k + cl * 8 < K;  // K % 8 == 0: a chunk is fully in or out
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                asrc[b] = or_zero(kin, ap[b] + k);
-                bsrc[b] = or_zero(kin, bp[b] + k);
+                asrc[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
+                bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
             }
         } else {
             ExtraStep x{};
@@ -926,7 +930,9 @@ hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm
         }
         if (g.bm == 256) {
             const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
-            auto ker = (L.adapters && !f.ext) ? gemm_dma_kernel<true> : gemm_dma_kernel<false>;
+            const bool epi = L.adapters && !f.ext, ktail = K % 32 != 0;
+            auto ker = epi ? (ktail ? gemm_dma_kernel<true, true> : gemm_dma_kernel<true, false>)
+                           : (ktail ? gemm_dma_kernel<false, true> : gemm_dma_kernel<false, false>);
             return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(512), st, L.X, L.W, L.Y, M, N, K, tiles_m,
                           tiles_n, f);
         }
