@@ -83,7 +83,7 @@ def measured_traffic(kernel):
     with open(path) as f:
         t = json.load(f)
     src = b"".join(open(os.path.join(ROOT, "rank_gemm_amd", "csrc", n), "rb").read()
-                   for n in ("gemm_bf16.hip", "shrink.h", "common.h", "kernels.h"))
+                   for n in ("splitk.hip", "fuse.h", "shrink.h", "common.h", "kernels.h"))
     if t.get("kernel") != kernel or hashlib.sha256(src).hexdigest() != t.get("sources_sha256"):
         return None
     return int(t["bytes_per_launch"])

@@ -1,0 +1,251 @@
+// Device pieces shared by the bf16 GEMM kernels of liblora: the fused
+// correction's arguments and slot metadata, the row scatter of the output,
+// the XCD-aware tile order, and the direct-to-LDS load helpers.
+//
+// The correction follows "LoRA serving, embeddings, rerankers, pooling"
+// (mlinterviewnotes.com, opening section): base GEMM once over the batch,
+// then the per-row indexed low-rank correction scale_s * (x A_s^T) B_s^T.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace lora {
+
+static inline __host__ __device__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+constexpr int kBK = 64;
+constexpr int kThreads = 256;
+
+struct Fuse {
+    const int32_t* token_order;  // sorted position -> token row
+    const int32_t* slot_indptr;  // [S+1]
+    const float* h;              // h_splits planes of [T][r_max], sorted positions, unscaled
+    const uint16_t* B_pool;      // [S][N][r_max]
+    const int32_t* rank;
+    const float* scale;
+    int S, r_max;
+    int h_splits;     // planes of h to add (1 when the shrink produced final h)
+    int64_t h_plane;  // elements per plane
+    int adapters;     // 0: no adapter row in the batch, skip the correction
+    const uint16_t* ext;  // tiled path: scaled h as bf16 hi / lo rows [T][2][rp], or null
+    int rp;               // r_max rounded up to 8
+};
+
+// Slot metadata (segment offsets, ranks, scales) staged in LDS at kernel
+// start, so the epilogue's slot walk does not chain global-memory latencies.
+// Pools with more than kMetaSlots slots read it from global memory instead.
+constexpr int kMetaSlots = 1024;
+struct SlotMeta {
+    int indptr[kMetaSlots + 1];
+    int rank[kMetaSlots];
+    float scale[kMetaSlots];
+};
+
+struct MetaView {
+    const int* indptr;
+    const int* rank;
+    const float* scale;
+};
+
+// Cooperative copy by every thread of the block; call before a barrier.
+__device__ __forceinline__ MetaView stage_meta(const Fuse& f, SlotMeta* sm) {
+    if (!f.adapters || f.S > kMetaSlots) return MetaView{f.slot_indptr, f.rank, f.scale};
+    for (int i = threadIdx.x; i <= f.S; i += blockDim.x) {
+        sm->indptr[i] = f.slot_indptr[i];
+        if (i < f.S) {
+            sm->rank[i] = f.rank[i];
+            sm->scale[i] = f.scale[i];
+        }
+    }
+    return MetaView{sm->indptr, sm->rank, sm->scale};
+}
+
+// 16-byte LDS chunk of (row, logical chunk c in 0..7). The XOR spreads the
+// 16 rows one MFMA operand read touches over distinct banks.
+__device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
+
+// Last slot s with slot_indptr[s] <= p (the slot whose segment holds p).
+__device__ __forceinline__ int slot_of(const int* indptr, int S, int p) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (indptr[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// acc[i][j] covers sorted rows p0 + 16 i + (4 (lane/16) + e) and columns
+// n0 + 16 j + lane % 16. Adds scale_s * h[p] . B_s[n] for every adapter row.
+template <int FM, int FN>
+__device__ __forceinline__ void fused_expand(f32x4 (&acc)[FM][FN], const Fuse& f, const MetaView& mv, int p0,
+                                             int n0, int M, int N, int lane) {
+    const int pend = min(M, p0 + FM * 16);
+    if (!f.adapters || p0 >= pend) return;
+    const int col = lane & 15, qg = lane >> 4;
+    const bool vec = (f.r_max & 3) == 0;
+    for (int s = slot_of(mv.indptr, f.S, p0); s < f.S; ++s) {
+        const int sb = mv.indptr[s], se = mv.indptr[s + 1];
+        if (sb >= pend) break;
+        const int r = mv.rank[s];
+        if (s == 0 || r == 0 || se <= p0 || se <= sb) continue;
+        const float sc = mv.scale[s];
+        const uint16_t* bs = f.B_pool + (int64_t)s * N * f.r_max;
+        const int nq = (r + 15) >> 4;
+        for (int qs = 0; qs < nq; ++qs) {
+            const int q = qs * 16 + qg * 4;
+            u32x2 bfr[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + j * 16 + col;
+                const uint16_t* src = bs + (int64_t)n * f.r_max + q;
+                if (vec) {  // B is zero past r inside the padded row
+                    bfr[j] = (n < N && q < r) ? *(const u32x2*)src : u32x2{0, 0};
+                } else {
+                    uint16_t e4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) e4[e] = (n < N && q + e < r) ? src[e] : uint16_t(0);
+                    bfr[j] = u32x2{uint32_t(e4[0]) | (uint32_t(e4[1]) << 16),
+                                   uint32_t(e4[2]) | (uint32_t(e4[3]) << 16)};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int bb = p0 + i * 16;
+                if (bb >= se || bb + 16 <= sb) continue;  // block outside the segment (uniform)
+                const int p = bb + col;                   // this lane's row of the A operand
+                const bool in = p >= sb && p < se;
+                float hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = 0.f;
+                    if (in && q + e < r) {
+                        const float* hp = f.h + (int64_t)p * f.r_max + q + e;
+                        for (int z = 0; z < f.h_splits; ++z) v += hp[z * f.h_plane];
+                        v *= sc;
+                    }
+                    hi[e] = bf16_to_f32(f32_to_bf16(v));
+                    lo[e] = v - hi[e];
+                }
+                const u32x2 ahi{pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+                const u32x2 alo{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    acc[i][j] = mfma16x16x16(ahi, bfr[j], acc[i][j]);
+                    acc[i][j] = mfma16x16x16(alo, bfr[j], acc[i][j]);
+                }
+            }
+        }
+    }
+}
+
+// Round and store: y[token_order[p]][n] for the rows and columns of acc.
+template <int FM, int FN>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], uint16_t* __restrict__ Y,
+                                           const int32_t* __restrict__ token_order, int p0, int n0, int M, int N,
+                                           int lane) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int p = p0 + i * 16 + (lane >> 4) * 4 + e;
+            if (p >= M) continue;
+            uint16_t* yr = Y + (int64_t)token_order[p] * N;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + j * 16 + (lane & 15);
+                if (n < N) yr[n] = f32_to_bf16(acc[i][j][e]);
+            }
+        }
+}
+
+// Map a linear block id to (tile_m, tile_n). Consecutive ids go round-robin
+// over the 8 XCDs, so ids are first regrouped so that each XCD owns one
+// contiguous run of tiles; inside a run tiles are ordered in groups of 8
+// tile-rows so that concurrently running tiles share x rows and W rows in
+// that XCD's L2.
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int nt = tiles_m * tiles_n;
+    int t = bid;
+    if ((nt & 7) == 0) t = (bid & 7) * (nt >> 3) + (bid >> 3);
+    constexpr int G = 8;
+    const int per_group = G * tiles_n;
+    const int g = t / per_group;
+    const int first = g * G;
+    const int gsize = min(tiles_m - first, G);
+    const int in = t - g * per_group;
+    tm = first + in % gsize;
+    tn = in / gsize;
+}
+
+// The expand as extra K steps of the tiled GEMM. For each slot s whose
+// segment meets the tile's rows [m0, mend) the K dimension is extended by
+// 2 rp (rp = r_max rounded up to 8): the A operand of row p is its ext row
+// [bf16 hi of scale_s h | lo remainder] (zero for rows of other segments),
+// the B operand of column n is [B_s[n] | B_s[n]], so the products add
+// scale_s h . B_s. The extension is walked in steps of 64 (or 32).
+struct ExtraStep {
+    int s, sb, se, r, t;
+};
+
+// Number of extra steps of `step` k (e < 0) or the decoding of step e.
+__device__ __forceinline__ int extra_steps(const MetaView& mv, const Fuse& f, int m0, int mend, int e,
+                                           ExtraStep* out, int step = 64) {
+    int n = 0;
+    for (int s = slot_of(mv.indptr, f.S, m0); s < f.S; ++s) {
+        const int sb = mv.indptr[s], se = mv.indptr[s + 1];
+        if (sb >= mend) break;
+        const int r = mv.rank[s];
+        if (s == 0 || r == 0 || se <= m0 || se <= sb) continue;
+        const int k = (2 * f.rp + step - 1) / step;
+        if (e >= 0 && e < n + k) {
+            *out = ExtraStep{s, sb, se, r, e - n};
+            return e;
+        }
+        n += k;
+    }
+    return n;
+}
+
+// ------------------------------------------------- direct-to-LDS loads --
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
+
+__device__ __forceinline__ void dma16(gptr<u32x4> src, u32x4* lds_dst) {
+    __builtin_amdgcn_global_load_lds((gptr<void>)src, (lds_void_ptr)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_offset(const u32x4* p) { return (uint32_t)(uintptr_t)(lds_u32x4_ptr)p; }
+
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+    return r;
+}
+// at most N LDS reads of this wave still outstanding; ties the wait to the
+// fragment registers so that no use of them moves above it
+template <int N>
+__device__ __forceinline__ void lds_landed(u32x4& a) {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_landed(u32x4& a, u32x4& b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+// at most N vector-memory ops of this wave outstanding, no LDS op
+template <int N>
+__device__ __forceinline__ void vm_landed() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The split-K decode path (kernel 1 + kernel 2), defined in splitk.hip.
+hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, Fuse f, hipStream_t st, StageTimer* tm);
+
+}  // namespace lora
