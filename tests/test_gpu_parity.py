@@ -165,6 +165,7 @@ EDGE = [
     (4000, 136, 4100, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # 256 x 256 tiles: ragged T, d_out, d_in; 5 extension steps
     (3900, 264, 4200, 4, [0, 3, 5, 2], 5, "bf16"),          # 256 x 256 tiles, r_max % 8 != 0: epilogue expand
     (4100, 256, 4000, 5, [0, 7, 2, 0, 6], 7, "bf16"),       # 256 x 256 tiles, epilogue expand, K % 32 == 0
+    (64, 40960, 256, 2, [0, 16], 16, "bf16"),               # split-K, 20 GEMM splits, one adapter
 ]
 
 
