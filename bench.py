@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-slices", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 256 MiB device copies (reference for the FETCH_SIZE/WRITE_SIZE counters)")
@@ -113,7 +114,7 @@ def main():
 
     from rank_gemm_amd import accounting as acc
     from rank_gemm_amd import lora
-    from rank_gemm_amd.inputs import make_config
+    from rank_gemm_amd.inputs import make_config, make_qkv_decode
 
     lora.lib()  # fail loudly if the library was not built
     if not torch.cuda.is_available():
@@ -231,6 +232,71 @@ def main():
                    "count": v["count"]} for k, v in stats.items()}
     log(f"kernels: {kernels}; base-only: {stats_base}")
 
+    # ---- q/k/v in one call against three calls ----------------------------------
+    slices = None
+    if not args.no_slices:
+        LQ = 8  # 8 layers of q/k/v weights (384 MiB) so the replays stream from HBM
+        with ThreadPoolExecutor(8) as ex:
+            qkv_host = list(ex.map(lambda l: make_qkv_decode(layer=l), range(LQ)))
+        qkv = []
+        for w in qkv_host:
+            pls = []
+            for pr in w.projections:
+                pl = lora.Pool(w.S, w.r_max, pr.d_in, pr.d_out, "bf16")
+                for s_, a in sorted(pr.adapters.items()):
+                    pl.install(s_, lora.to_device(a.A, "bf16"), lora.to_device(a.B, "bf16"), a.alpha)
+                pls.append(pl)
+            qkv.append((lora.to_device(w.projections[0].x, "bf16"), [lora.to_device(pr.W, "bf16") for pr in w.projections],
+                        pls, [torch.empty((w.T, pr.d_out), dtype=torch.bfloat16, device="cuda")
+                              for pr in w.projections]))
+        wq = qkv_host[0]
+        pq = lora.plan(wq.slot_ids, wq.S)
+        wsq = torch.empty(max(lora.workspace_bytes_multi(qkv[0][2], wq.T),
+                              max(pl.workspace_bytes(wq.T) for pl in qkv[0][2])), dtype=torch.uint8, device="cuda")
+
+        def merged():
+            for x_, W_, pl_, y_ in qkv:
+                lora.linear_multi(x_, W_, pl_, pq, ys=y_, workspace=wsq)
+
+        def separate():
+            for x_, W_, pl_, y_ in qkv:
+                for i in range(3):
+                    lora.linear(x_, W_[i], pl_[i], pq, y=y_[i], workspace=wsq)
+
+        def time_graph(fn, reps=20):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * LQ)
+
+        us_m, us_s = time_graph(merged), time_graph(separate)
+        rq = wq.ranks
+        outs = [pr.d_out for pr in wq.projections]
+        a_q = sum(2 * int(rq[s_]) * d_in for s_ in acc.segments(wq.slot_ids, rq))
+        b_q = sum(2 * int(rq[s_]) * n for s_ in acc.segments(wq.slot_ids, rq) for n in outs)
+        lay_bytes = 2 * wq.T * d_in + sum(2 * d_in * n + 2 * wq.T * n for n in outs) + 3 * a_q + b_q
+        slices = {"workload": f"llama3-8b q/k/v decode: T={wq.T}, {d_in}->{outs}, S={wq.S} rank 16, {LQ} layers",
+                  "merged_us_per_layer": round(us_m, 3), "separate_us_per_layer": round(us_s, 3),
+                  "speedup": round(us_s / us_m, 3), "bytes_per_layer": lay_bytes,
+                  "merged_frac_hbm": round(lay_bytes / (us_m * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"slices: {slices}")
+        del qkv, wsq
+
     # ---- prefill-shaped base GEMM (matrix-core fraction) --------------------------
     prefill = None
     if not args.no_prefill:
@@ -311,7 +377,7 @@ def main():
                    "T": T, "d_in": d_in, "d_out": d_out, "S": S, "rank": 16, "layers": L,
                    "mode": "eager" if graph is None else "hip graph replay"},
         "roofline": roof, "cpu_baseline": cpu,
-        "correction": corr, "kernels": kernels, "prefill": prefill,
+        "correction": corr, "kernels": kernels, "prefill": prefill, "slices": slices,
     }
     print(json.dumps(out), flush=True)
 

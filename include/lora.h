@@ -169,6 +169,46 @@ int lora_linear(const lora_pool* pool, const void* x, const void* W, const int32
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Several adapted projections that read the same x (a merged q/k/v or
+ * gate/up wrapper), in one call: the "output slices" that one shrink and one
+ * expand launch cover in "LoRA serving, embeddings, rerankers, pooling"
+ * (mlinterviewnotes.com), section "vLLM: preallocated stacked buffers plus a
+ * Punica-style Triton kernel". Each slice has its own base weight, output
+ * and adapter pool; all slices share x and the plan, so slot s means the
+ * same adapter identity in every slice's pool (each pool may hold its own
+ * rank for it).
+ *   slices       host [n], 1 <= n <= LORA_MAX_SLICES; every pool has the same
+ *                S, r_max, d_in and element type; slice i writes
+ *                y_i = x W_i^T + per-row correction from slices[i].pool,
+ *                exactly what lora_linear(slices[i].pool, x, W_i, ..., y_i)
+ *                defines (to fp32 rounding order for bf16 pools: split points
+ *                of K may differ)
+ *   x, token_order, slot_indptr, work, info, stream: as lora_linear
+ *   workspace    dev, at least lora_workspace_bytes_multi(slices, n, T) bytes
+ * With bf16 pools, slices whose concatenated columns fall on the decode
+ * (split-K) path are computed by one GEMM launch and one epilogue launch
+ * between them, x being read once per K split for all slices; otherwise the
+ * slices run one after another. No y may alias x, any W or another y.
+ * Errors: LORA_EINVAL (n out of range, pools that differ, null pointer,
+ * aliasing), LORA_ESPACE, LORA_EHIP.
+ */
+#define LORA_MAX_SLICES 4
+
+typedef struct lora_slice {
+    const lora_pool* pool; /* adapters of this projection, d_out columns */
+    const void* W;         /* dev [pool d_out][d_in] */
+    void* y;               /* dev [T][pool d_out] out */
+} lora_slice;
+
+/* Device workspace of lora_linear_multi over these pools (slices[i].W and
+ * .y are not read); 0 when the pools cannot share a call. */
+size_t lora_workspace_bytes_multi(const lora_slice* slices, int n, int T);
+
+int lora_linear_multi(const lora_slice* slices, int n, const void* x, const int32_t* token_order,
+                      const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The shrink alone, for inspection: h dev fp32 [T][r_max] receives
  * h[t][q] = sum_k x[t,k] A_s[q,k] for q < r_s, and 0 for q >= r_s and for
  * rows on slot 0 or a rank-0 slot (the "[tokens, r]-shaped" intermediate of

@@ -36,7 +36,39 @@ inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 inline size_t h_bytes(const lora_pool* p, int T) {
     const size_t h = align256((size_t)T * p->r_max * sizeof(float));
     if (p->dtype != LORA_BF16) return h;
-    const size_t g = lora::gemm_bf16_workspace(T, p->d_out, p->d_in, p->r_max);
+    const size_t g = lora::gemm_bf16_workspace(T, &p->d_out, 1, p->d_in, p->r_max);
+    return g > h ? g : h;
+}
+
+static_assert(LORA_MAX_SLICES == lora::kMaxSlices, "slice limit of the interface and the kernels");
+
+// Every slice's pool must agree with the first on S, r_max, d_in and element
+// type; with buffers, no output may alias x, a weight or another output.
+int check_slices(const lora_slice* sl, int n, const void* x, bool buffers) {
+    if (!sl || n < 1 || n > LORA_MAX_SLICES) return LORA_EINVAL;
+    const lora_pool* p0 = sl[0].pool;
+    for (int i = 0; i < n; ++i) {
+        const lora_pool* p = sl[i].pool;
+        if (!p) return LORA_EINVAL;
+        if (p->S != p0->S || p->r_max != p0->r_max || p->d_in != p0->d_in || p->dtype != p0->dtype)
+            return LORA_EINVAL;
+        if (!buffers) continue;
+        if (!sl[i].W || !sl[i].y || sl[i].y == x) return LORA_EINVAL;
+        for (int j = 0; j < n; ++j) {
+            if (sl[i].y == sl[j].W) return LORA_EINVAL;
+            if (j != i && sl[i].y == sl[j].y) return LORA_EINVAL;
+        }
+    }
+    return LORA_OK;
+}
+
+size_t multi_bytes(const lora_slice* sl, int n, int T) {
+    const lora_pool* p0 = sl[0].pool;
+    const size_t h = align256((size_t)T * p0->r_max * sizeof(float));
+    if (p0->dtype != LORA_BF16) return h;
+    int N[LORA_MAX_SLICES];
+    for (int i = 0; i < n; ++i) N[i] = sl[i].pool->d_out;
+    const size_t g = lora::gemm_bf16_workspace(T, N, n, p0->d_in, p0->r_max);
     return g > h ? g : h;
 }
 
@@ -226,10 +258,21 @@ int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t*
 
     if (p->dtype == LORA_BF16) {
         if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
-        const lora::LinearArgs la{(const uint16_t*)x, (const uint16_t*)W, (uint16_t*)y, T, p->d_out, p->d_in,
-                                  token_order, slot_indptr, work, info->n_items, (const uint16_t*)p->A,
-                                  (const uint16_t*)p->B, p->rank_dev, p->scale_dev, p->S, p->r_max,
-                                  adapters ? 1 : 0, workspace};
+        lora::LinearArgs la{};
+        la.X = (const uint16_t*)x;
+        la.M = T;
+        la.K = p->d_in;
+        la.token_order = token_order;
+        la.slot_indptr = slot_indptr;
+        la.work = work;
+        la.n_items = info->n_items;
+        la.S = p->S;
+        la.r_max = p->r_max;
+        la.adapters = adapters ? 1 : 0;
+        la.workspace = workspace;
+        la.n_slices = 1;
+        la.slice[0] = {(const uint16_t*)W, (uint16_t*)y, p->d_out, (const uint16_t*)p->A, (const uint16_t*)p->B,
+                       p->rank_dev, p->scale_dev};
         return lora::lora_forward_bf16(la, st, tm) == hipSuccess ? LORA_OK : LORA_EHIP;
     }
     if (lora::gemm_f32((const float*)x, (const float*)W, (float*)y, T, p->d_out, p->d_in, st, tm) != hipSuccess)
@@ -242,6 +285,58 @@ int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t*
                               (float*)y, p->d_out, p->r_max, st, tm) != hipSuccess)
         return LORA_EHIP;
     return LORA_OK;
+}
+
+size_t lora_workspace_bytes_multi(const lora_slice* slices, int n, int T) {
+    if (T < 0 || check_slices(slices, n, nullptr, false) != LORA_OK) return 0;
+    return multi_bytes(slices, n, T);
+}
+
+int lora_linear_multi(const lora_slice* slices, int n, const void* x, const int32_t* token_order,
+                      const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_slices(slices, n, x, true);
+    if (rc != LORA_OK) return rc;
+    const lora_pool* p0 = slices[0].pool;
+    rc = check_plan(p0, token_order, slot_indptr, work, info);
+    if (rc != LORA_OK) return rc;
+    const int T = info->T;
+    if (T == 0) return LORA_OK;
+    if (!x) return LORA_EINVAL;
+    if (p0->dtype != LORA_BF16) {
+        // fp32 pools: the slices one after another on the same stream (the
+        // workspace is reused in stream order)
+        for (int i = 0; i < n; ++i) {
+            rc = lora_linear(slices[i].pool, x, slices[i].W, token_order, slot_indptr, work, info, slices[i].y,
+                             workspace, workspace_bytes, stream);
+            if (rc != LORA_OK) return rc;
+        }
+        return LORA_OK;
+    }
+    if (!workspace || workspace_bytes < multi_bytes(slices, n, T)) return LORA_ESPACE;
+    hipStream_t st = as_stream(stream);
+    std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
+    if (profiler().on) lk.lock();
+    lora::StageTimer* tm = timer_for(st);
+    lora::LinearArgs la{};
+    la.X = (const uint16_t*)x;
+    la.M = T;
+    la.K = p0->d_in;
+    la.token_order = token_order;
+    la.slot_indptr = slot_indptr;
+    la.work = work;
+    la.n_items = info->n_items;
+    la.S = p0->S;
+    la.r_max = p0->r_max;
+    la.adapters = info->T_a > 0 && info->n_items > 0 ? 1 : 0;
+    la.workspace = workspace;
+    la.n_slices = n;
+    for (int i = 0; i < n; ++i) {
+        const lora_pool* p = slices[i].pool;
+        la.slice[i] = {(const uint16_t*)slices[i].W, (uint16_t*)slices[i].y, p->d_out, (const uint16_t*)p->A,
+                       (const uint16_t*)p->B, p->rank_dev, p->scale_dev};
+    }
+    return lora::lora_forward_bf16(la, st, tm) == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
 int lora_shrink(const lora_pool* p, const void* x, const int32_t* token_order, const int32_t* slot_indptr,

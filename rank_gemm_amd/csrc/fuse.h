@@ -245,7 +245,9 @@ __device__ __forceinline__ void stage_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The split-K decode path (kernel 1 + kernel 2), defined in splitk.hip.
-hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, Fuse f, hipStream_t st, StageTimer* tm);
+// The split-K decode path (kernel 1 + kernel 2) over every slice of L
+// together, defined in splitk.hip. `g` is the plan of the slices'
+// concatenated columns (its n_nt is recomputed per slice).
+hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, hipStream_t st, StageTimer* tm);
 
 }  // namespace lora

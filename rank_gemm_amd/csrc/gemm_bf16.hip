@@ -322,15 +322,49 @@ GemmPlan gemm_bf16_plan(int M, int N, int K) {
     return g;
 }
 
-size_t gemm_bf16_workspace(int M, int N, int K, int r_max) {
-    if (M <= 0 || N <= 0 || K <= 0) return 0;
-    const GemmPlan g = gemm_bf16_plan(M, N, K);
-    // fp32 h [M][r_max], or bf16 hi / lo [M][2][round_up(r_max, 8)]
-    const size_t h_final = (size_t)M * ((r_max + 7) & ~7) * sizeof(float);
-    if (g.nsub == 0) return (h_final + 255) & ~size_t(255);
-    const size_t py = (size_t)g.ks * g.n_mt * g.n_nt * 16 * 64 * 16;
-    const size_t ph = (size_t)g.hs * M * r_max * sizeof(float);
+// Workspace of the split-K pass over all slices together.
+static size_t split_workspace(int M, int n_nt_total, const GemmPlan& g, int n_slices, int r_max) {
+    const size_t py = (size_t)g.ks * g.n_mt * n_nt_total * 16 * 64 * 16;
+    const size_t ph = (size_t)n_slices * g.hs * M * r_max * sizeof(float);
     return ((py + 255) & ~size_t(255)) + ((ph + 255) & ~size_t(255));
+}
+
+static int total_tiles_n(const int* N, int n_slices) {
+    int t = 0;
+    for (int i = 0; i < n_slices; ++i) t += cdiv(N[i], 64);
+    return t;
+}
+
+// Slices share one pass when their concatenated columns take the split-K
+// path; otherwise each slice runs on its own (tiled or split-K).
+static bool joint_split(int M, const int* N, int n_slices, int K, GemmPlan* out) {
+    int n_total = 0;
+    for (int i = 0; i < n_slices; ++i) n_total += N[i];
+    const GemmPlan g = gemm_bf16_plan(M, n_total, K);
+    if (out) *out = g;
+    return g.nsub != 0;
+}
+
+size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max) {
+    if (M <= 0 || K <= 0 || n_slices < 1) return 0;
+    GemmPlan gj;
+    if (n_slices > 1 && joint_split(M, N, n_slices, K, &gj)) {
+        // the joint plan's tiles are those of the concatenated columns;
+        // count whole 64-column tiles per slice
+        GemmPlan g = gj;
+        g.n_nt = total_tiles_n(N, n_slices);
+        return split_workspace(M, g.n_nt, g, n_slices, r_max);
+    }
+    size_t need = 0;
+    for (int i = 0; i < n_slices; ++i) {
+        if (N[i] <= 0) continue;
+        const GemmPlan g = gemm_bf16_plan(M, N[i], K);
+        // fp32 h [M][r_max], or bf16 hi / lo [M][2][round_up(r_max, 8)]
+        const size_t h_final = (size_t)M * ((r_max + 7) & ~7) * sizeof(float);
+        const size_t b = g.nsub == 0 ? ((h_final + 255) & ~size_t(255)) : split_workspace(M, g.n_nt, g, 1, r_max);
+        need = b > need ? b : need;
+    }
+    return need;
 }
 
 template <int BM, int BN>
@@ -341,38 +375,58 @@ static hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y
                   M, N, K, tiles_m, tiles_n, f);
 }
 
-hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {
-    const int M = L.M, N = L.N, K = L.K;
-    if (M == 0 || N == 0) return hipSuccess;
-    const GemmPlan g = gemm_bf16_plan(M, N, K);
-    Fuse f{L.token_order, L.slot_indptr, nullptr, L.B_pool, L.rank, L.scale, L.S, L.r_max, 1, 0, L.adapters,
+// One slice on the tiled path: the shrink to final h, then the tiled GEMM
+// with the expand fused (r_max % 8 == 0: as extra K steps from scaled h as
+// bf16 hi / lo; otherwise in the epilogue from fp32 h).
+static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
+                                StageTimer* tm) {
+    const int M = L.M, N = sl.N, K = L.K;
+    Fuse f{L.token_order, L.slot_indptr, nullptr, sl.B_pool, sl.rank, sl.scale, L.S, L.r_max, 1, 0, L.adapters,
            nullptr, (L.r_max + 7) & ~7};
     char* ws = static_cast<char*>(L.workspace);
-    if (g.nsub == 0) {
-        // shrink to final h, then the tiled GEMM with the expand in its epilogue
-        // r_max % 8 == 0: the expand runs as extra K steps (operand: scaled
-        // h as bf16 hi / lo); otherwise in the epilogue from fp32 h
-        float* hbuf = reinterpret_cast<float*>(ws);
-        uint16_t* ext = (L.r_max % 8 == 0) ? reinterpret_cast<uint16_t*>(ws) : nullptr;
-        f.h = ext ? nullptr : hbuf;
-        f.ext = ext;
-        if (L.adapters) {
-            const hipError_t e = sgmv_shrink(1, L.X, L.A_pool, L.rank, L.token_order, L.work, L.n_items,
-                                             ext ? nullptr : hbuf, K, L.r_max, st, tm, L.scale, ext);
-            if (e != hipSuccess) return e;
-        }
-        if (g.bm == 256) {
-            const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
-            const bool epi = L.adapters && !f.ext, ktail = K % 32 != 0;
-            auto ker = epi ? (ktail ? gemm_dma_kernel<true, true> : gemm_dma_kernel<true, false>)
-                           : (ktail ? gemm_dma_kernel<false, true> : gemm_dma_kernel<false, false>);
-            return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(512), st, L.X, L.W, L.Y, M, N, K, tiles_m,
-                          tiles_n, f);
-        }
-        if (g.bm == 128) return launch_tiled<128, 128>(L.X, L.W, L.Y, M, N, K, f, st, tm);
-        return launch_tiled<64, 128>(L.X, L.W, L.Y, M, N, K, f, st, tm);
+    float* hbuf = reinterpret_cast<float*>(ws);
+    uint16_t* ext = (L.r_max % 8 == 0) ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+    f.h = ext ? nullptr : hbuf;
+    f.ext = ext;
+    if (L.adapters) {
+        const hipError_t e = sgmv_shrink(1, L.X, sl.A_pool, sl.rank, L.token_order, L.work, L.n_items,
+                                         ext ? nullptr : hbuf, K, L.r_max, st, tm, sl.scale, ext);
+        if (e != hipSuccess) return e;
     }
-    return splitk_forward_bf16(L, g, f, st, tm);
+    if (g.bm == 256) {
+        const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
+        const bool epi = L.adapters && !f.ext, ktail = K % 32 != 0;
+        auto ker = epi ? (ktail ? gemm_dma_kernel<true, true> : gemm_dma_kernel<true, false>)
+                       : (ktail ? gemm_dma_kernel<false, true> : gemm_dma_kernel<false, false>);
+        return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(512), st, L.X, sl.W, sl.Y, M, N, K,
+                      tiles_m, tiles_n, f);
+    }
+    if (g.bm == 128) return launch_tiled<128, 128>(L.X, sl.W, sl.Y, M, N, K, f, st, tm);
+    return launch_tiled<64, 128>(L.X, sl.W, sl.Y, M, N, K, f, st, tm);
+}
+
+hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {
+    const int M = L.M, K = L.K, n = L.n_slices;
+    if (M == 0 || n < 1) return hipSuccess;
+    int N[kMaxSlices];
+    for (int i = 0; i < n; ++i) N[i] = L.slice[i].N;
+    GemmPlan gj;
+    if (n > 1 && joint_split(M, N, n, K, &gj)) return splitk_forward_bf16(L, gj, st, tm);
+    for (int i = 0; i < n; ++i) {
+        if (N[i] == 0) continue;
+        const GemmPlan g = gemm_bf16_plan(M, N[i], K);
+        hipError_t e;
+        if (g.nsub == 0) {
+            e = tiled_forward(L, L.slice[i], g, st, tm);
+        } else {
+            LinearArgs one = L;
+            one.n_slices = 1;
+            one.slice[0] = L.slice[i];
+            e = splitk_forward_bf16(one, g, st, tm);
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace lora

@@ -37,6 +37,8 @@ inline hipError_t launch(StageTimer* tm, const char* name, void (*kernel)(Params
 // ---- bf16 forward: shrink + base GEMM with the expand in its epilogue ------
 // y[token_order[p]] = bf16(x[token_order[p]] W^T + scale_s h[p] B_s^T), rows
 // visited in plan order; with adapters == 0 the correction is skipped.
+// Several slices (projections reading the same x, each with its own W, y and
+// pool) can be computed in one pass.
 struct GemmPlan {
     int bm, bn;          // macro tile of the tiled path
     int nsub;            // split-K path: 128-wide K sub-chunks per split (0 = tiled path)
@@ -44,25 +46,33 @@ struct GemmPlan {
     int hs, hkc;         // split-K path: shrink splits of hkc k each (hkc % 32 == 0)
 };
 GemmPlan gemm_bf16_plan(int M, int N, int K);
-size_t gemm_bf16_workspace(int M, int N, int K, int r_max);
+
+constexpr int kMaxSlices = 4;
+struct SliceArgs {
+    const uint16_t* W;       // [N][K]
+    uint16_t* Y;             // [M][N]
+    int N;
+    const uint16_t* A_pool;  // [S][r_max][K]
+    const uint16_t* B_pool;  // [S][N][r_max]
+    const int32_t* rank;     // [S]
+    const float* scale;      // [S]
+};
 
 struct LinearArgs {
-    const uint16_t* X;
-    const uint16_t* W;
-    uint16_t* Y;
-    int M, N, K;
+    const uint16_t* X;  // [M][K]
+    int M, K;
     const int32_t* token_order;
     const int32_t* slot_indptr;
     const int32_t* work;
     int n_items;
-    const uint16_t* A_pool;
-    const uint16_t* B_pool;
-    const int32_t* rank;
-    const float* scale;
     int S, r_max;
     int adapters;
     void* workspace;
+    int n_slices;
+    SliceArgs slice[kMaxSlices];
 };
+// workspace of a forward over slices of N[0..n_slices) columns
+size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max);
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm);
 hipError_t gemm_f32(const float* X, const float* W, float* Y, int M, int N, int K, hipStream_t st, StageTimer* tm);
 

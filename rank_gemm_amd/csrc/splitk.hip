@@ -9,29 +9,73 @@
 // shrink over the same K range in finer splits. Kernel 2 adds the partial
 // products in split order, applies the expand scale_s * h[p] B_s^T in fp32
 // and rounds once. No workgroup waits on another.
+//
+// Projections that read the same x (the output slices of a merged q/k/v or
+// gate/up wrapper, section "vLLM: preallocated stacked buffers plus a
+// Punica-style Triton kernel" of the same page) can share both launches:
+// their 64-column tiles are numbered one after the other, and each tile takes
+// the weight, output and adapter pool of the slice it falls in; the shrink
+// workgroups cover every slice's A over the same K splits. The MULTI template
+// flag keeps the one-slice kernels free of the slice lookup.
 #include "fuse.h"
 #include "shrink.h"
 
 namespace lora {
 
 // -------------------------------------------------------------- split-K --
+// The slices of one pass (projections reading the same x), their 64-column
+// tiles numbered one after the other: slice i owns tiles nt0[i] .. nt0[i+1).
+struct SliceTable {
+    int n;
+    int nt0[kMaxSlices + 1];
+    int N[kMaxSlices];
+    const uint16_t* W[kMaxSlices];
+    const uint16_t* A_pool[kMaxSlices];
+    const uint16_t* B_pool[kMaxSlices];
+    const int32_t* rank[kMaxSlices];
+    const float* scale[kMaxSlices];
+    uint16_t* Y[kMaxSlices];
+};
+
+// Entry i of a slice array, by selects (a dynamically indexed kernel
+// argument would be copied to scratch memory).
+template <class T>
+__device__ __forceinline__ T pick(const T (&v)[kMaxSlices], int i) {
+    T r = v[0];
+#pragma unroll
+    for (int j = 1; j < kMaxSlices; ++j) r = i == j ? v[j] : r;
+    return r;
+}
+
+__device__ __forceinline__ int nt_first(const SliceTable& t, int i) {
+    int r = t.nt0[0];
+#pragma unroll
+    for (int j = 1; j < kMaxSlices; ++j) r = i == j ? t.nt0[j] : r;
+    return r;
+}
+
+__device__ __forceinline__ int slice_of(const SliceTable& t, int nt) {
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxSlices; ++j) i += (j < t.n && nt >= t.nt0[j]) ? 1 : 0;
+    return i;
+}
+
 struct SplitArgs {
     const uint16_t* X;
-    const uint16_t* W;
-    float* part_y;  // [ks][n_mt][n_nt][16 fragments][64 lanes] f32x4
-    int M, N, K, n_mt, n_nt, ks;
-    // shrink workgroups (the first n_items * hs blocks), hkc k each
-    const uint16_t* A_pool;
-    const int32_t* rank;
+    float* part_y;  // [ks][n_mt][n_nt][16 fragments][64 lanes] f32x4, n_nt over all slices
+    int M, K, n_mt, n_nt, ks;
+    // shrink workgroups (the first n_items * hs * n blocks), hkc k each
     const int32_t* token_order;
     const Item* work;
     int n_items, r_max;
-    float* part_h;  // [hs][M][r_max]
+    float* part_h;  // [n][hs][M][r_max]
     int hs, hkc;
+    SliceTable sl;
 };
 
-// grid: n_items * hs shrink blocks, then n_mt * n_nt * ks GEMM blocks. The
-// shrink splits are finer than the GEMM's, so that they finish early.
+// grid: n_items * hs * n shrink blocks, then n_mt * n_nt * ks GEMM blocks.
+// The shrink splits are finer than the GEMM's, so that they finish early.
 // Wave w of a GEMM block owns columns n0 + 16 w .. + 15 of a 64 x 64 tile.
 // The split's x rows (gathered through token_order) and W rows stream
 // through kSplitStages LDS buffers of 64 k by direct-to-LDS loads: a stage is
@@ -43,19 +87,20 @@ struct SplitArgs {
 constexpr int kSplitStages = 5;
 constexpr int kSplitStageChunks = 1024;  // 16-byte chunks: x 512, W 512
 
-template <int NSUB>
+template <int NSUB, bool MULTI>
 __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
     __shared__ u32x4 lds[kSplitStages * kSplitStageChunks];  // 80 KB
     constexpr int KC = NSUB * 128, NST = NSUB * 2, NS = kSplitStages, SC = kSplitStageChunks;
-    const int n_shrink = a.n_items * a.hs;
+    const int n_shrink = a.n_items * a.hs * (MULTI ? a.sl.n : 1);
     if ((int)blockIdx.x < n_shrink) {
-        const int item = blockIdx.x % a.n_items, kz = blockIdx.x / a.n_items;
+        const int item = blockIdx.x % a.n_items, rest = blockIdx.x / a.n_items;
+        const int kz = MULTI ? rest % a.hs : rest, si = MULTI ? rest / a.hs : 0;
         const Item it = a.work[item];
-        const int r = a.rank[it.slot];
+        const int r = pick(a.sl.rank, si)[it.slot];
         if (r == 0) return;
         const int kbeg = kz * a.hkc, kend = min(a.K, kbeg + a.hkc);
-        const ShrinkOut out{a.part_h + (int64_t)kz * a.M * a.r_max, nullptr, 0, 0.f};
-        shrink_item<4>(a.X, a.A_pool, r, a.token_order, it, out, a.K, kbeg, kend, a.r_max,
+        const ShrinkOut out{a.part_h + ((int64_t)si * a.hs + kz) * a.M * a.r_max, nullptr, 0, 0.f};
+        shrink_item<4>(a.X, pick(a.sl.A_pool, si), r, a.token_order, it, out, a.K, kbeg, kend, a.r_max,
                        reinterpret_cast<f32x4*>(lds));
         return;
     }
@@ -64,7 +109,10 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
     const int kz = g / tiles, t = g - kz * tiles;
     const int mt = t / a.n_nt, nt = t - mt * a.n_nt;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int m0 = mt * 64, n0 = nt * 64;
+    const int si = MULTI ? slice_of(a.sl, nt) : 0;
+    const uint16_t* __restrict__ W = pick(a.sl.W, si);
+    const int N = pick(a.sl.N, si);
+    const int m0 = mt * 64, n0 = (nt - nt_first(a.sl, si)) * 64;
     const int kbeg = kz * KC;
     const int K = a.K;
     // this lane's rows and chunk in its two x and two W block loads
@@ -77,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
         const int r = 16 * wave + 8 * j + dr;  // tile row / column 0..63
         kc[j] = kbeg + (dc ^ (r & 7)) * 8;     // this lane's k within a stage
         xs[j] = a.X + (int64_t)a.token_order[min(m0 + r, a.M - 1)] * K + kc[j];
-        ws[j] = a.W + (int64_t)min(n0 + r, a.N - 1) * K + kc[j];
+        ws[j] = W + (int64_t)min(n0 + r, N - 1) * K + kc[j];
     }
     auto issue = [&](int s) {
         u32x4* st = lds + (s % NS) * SC;
@@ -140,18 +188,25 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
 // the last row's 32-rank reads in bounds; what they read there is not used).
 constexpr int kLaneMetaSlots = 64;
 
-template <bool ADAPT, bool VEC, bool LANE_META>
+template <bool ADAPT, bool VEC, bool LANE_META, bool MULTI>
 __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* __restrict__ part_y, int ks, int n_mt,
-                                                                   int n_nt, uint16_t* __restrict__ Y, int M, int N,
-                                                                   Fuse f) {
+                                                                   int n_nt, int M, Fuse f, SliceTable tab) {
     const int nt = blockIdx.x, mt = blockIdx.y >> 2, rb = blockIdx.y & 3;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int p0 = mt * 64 + rb * 16;
     if (p0 >= M) return;  // uniform for the block
+    // this tile's slice: its columns, output and pool
+    const int si = MULTI ? slice_of(tab, nt) : 0;
+    const int N = pick(tab.N, si);
+    uint16_t* __restrict__ Y = pick(tab.Y, si);
+    f.B_pool = pick(tab.B_pool, si);
+    f.rank = pick(tab.rank, si);
+    f.scale = pick(tab.scale, si);
+    if (ADAPT) f.h += (int64_t)si * f.h_splits * f.h_plane;
     const f32x4* in = reinterpret_cast<const f32x4*>(part_y);
     const int64_t zstride = (int64_t)n_mt * n_nt * 16 * 64;
     const int64_t o = (((int64_t)mt * n_nt + nt) * 16 + rb * 4 + w) * 64 + lane;
-    const int n = nt * 64 + w * 16 + (lane & 15);
+    const int n = (nt - nt_first(tab, si)) * 64 + w * 16 + (lane & 15);
     // splits are added in split order; loads are issued unconditionally from
     // clamped addresses (a load under a branch is waited on inside it) and
     // the extra ones are not added
@@ -341,17 +396,43 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
 
 template <int NSUB>
 static hipError_t launch_split(const SplitArgs& a, int n_blocks, hipStream_t st, StageTimer* tm) {
-    return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB>, dim3(n_blocks), dim3(kThreads), st, a);
+    return launch(tm, "gemm_splitk", a.sl.n > 1 ? splitk_gemm_kernel<NSUB, true> : splitk_gemm_kernel<NSUB, false>,
+                  dim3(n_blocks), dim3(kThreads), st, a);
 }
 
-hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, Fuse f, hipStream_t st, StageTimer* tm) {
-    const int M = L.M, N = L.N, K = L.K;
+template <bool MULTI>
+static auto epilogue_for(const LinearArgs& L) {
+    if (!L.adapters) return splitk_epilogue_kernel<false, false, false, MULTI>;
+    if (L.r_max % 8 != 0) return splitk_epilogue_kernel<true, false, false, MULTI>;
+    if (L.S <= kLaneMetaSlots) return splitk_epilogue_kernel<true, true, true, MULTI>;
+    return splitk_epilogue_kernel<true, true, false, MULTI>;
+}
+
+hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, hipStream_t st, StageTimer* tm) {
+    const int M = L.M, K = L.K, n = L.n_slices;
+    SliceTable sl{};
+    sl.n = n;
+    int nt = 0;
+    for (int i = 0; i < kMaxSlices; ++i) {
+        sl.nt0[i] = nt;
+        if (i >= n) continue;
+        const SliceArgs& s = L.slice[i];
+        sl.N[i] = s.N;
+        sl.W[i] = s.W;
+        sl.A_pool[i] = s.A_pool;
+        sl.B_pool[i] = s.B_pool;
+        sl.rank[i] = s.rank;
+        sl.scale[i] = s.scale;
+        sl.Y[i] = s.Y;
+        nt += cdiv(s.N, 64);
+    }
+    sl.nt0[kMaxSlices] = nt;
     char* ws = static_cast<char*>(L.workspace);
-    const size_t py = ((size_t)g.ks * g.n_mt * g.n_nt * 16 * 64 * 16 + 255) & ~size_t(255);
-    SplitArgs a{L.X, L.W, reinterpret_cast<float*>(ws), M, N, K, g.n_mt, g.n_nt, g.ks,
-                L.A_pool, L.rank, L.token_order, reinterpret_cast<const Item*>(L.work),
-                L.adapters ? L.n_items : 0, L.r_max, reinterpret_cast<float*>(ws + py), g.hs, g.hkc};
-    const int n_blocks = a.n_items * g.hs + g.n_mt * g.n_nt * g.ks;
+    const size_t py = ((size_t)g.ks * g.n_mt * nt * 16 * 64 * 16 + 255) & ~size_t(255);
+    SplitArgs a{L.X, reinterpret_cast<float*>(ws), M, K, g.n_mt, nt, g.ks, L.token_order,
+                reinterpret_cast<const Item*>(L.work), L.adapters ? L.n_items : 0, L.r_max,
+                reinterpret_cast<float*>(ws + py), g.hs, g.hkc, sl};
+    const int n_blocks = a.n_items * g.hs * n + g.n_mt * nt * g.ks;
     hipError_t e;
     switch (g.nsub) {
         case 1: e = launch_split<1>(a, n_blocks, st, tm); break;
@@ -361,19 +442,14 @@ hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, Fuse f, h
         default: e = launch_split<16>(a, n_blocks, st, tm); break;
     }
     if (e != hipSuccess) return e;
-    f.h = a.part_h;
-    f.h_splits = g.hs;
-    f.h_plane = (int64_t)M * L.r_max;
-    const dim3 eg(g.n_nt, 4 * g.n_mt);
-    auto epi = splitk_epilogue_kernel<false, false, false>;
-    if (L.adapters) {
-        if (L.r_max % 8 != 0) epi = splitk_epilogue_kernel<true, false, false>;
-        else if (L.S <= kLaneMetaSlots) epi = splitk_epilogue_kernel<true, true, true>;
-        else epi = splitk_epilogue_kernel<true, true, false>;
-    }
+    // per-slice pool pointers and h planes are set by each kernel-2 block
+    const Fuse f{L.token_order, L.slot_indptr, a.part_h, nullptr, nullptr, nullptr, L.S, L.r_max, g.hs,
+                 (int64_t)M * L.r_max, L.adapters, nullptr, (L.r_max + 7) & ~7};
+    const dim3 eg(nt, 4 * g.n_mt);
+    auto epi = n > 1 ? epilogue_for<true>(L) : epilogue_for<false>(L);
     const uint32_t shm = L.adapters ? (uint32_t)((16 * L.r_max + 32) * sizeof(float)) : 0u;
     return launch_shm(tm, "gemm_splitk_epilogue", epi, eg, dim3(kThreads), shm, st, (const float*)a.part_y, g.ks,
-                      g.n_mt, g.n_nt, L.Y, M, N, f);
+                      g.n_mt, nt, M, f, sl);
 }
 
 }  // namespace lora

@@ -225,3 +225,42 @@ def make_custom(seed, T, d_in, d_out, S, ranks, alphas, slot_ids, dtype=BF16, r_
             pool.shutdown()
     rm = int(r_max if r_max is not None else max(1, int(ranks.max(initial=0))))
     return Workload("custom", dtype, T, S, rm, slot_ids, [p])
+
+
+def make_slices(seed, T, d_in, d_outs, S, ranks, alphas, slot_ids, dtype=BF16, r_max=None, names=None,
+                pool=None) -> Workload:
+    """Several projections that read one x (a merged q/k/v or gate/up): one
+    projection per entry of ``d_outs``, each with its own base weight and its
+    own adapters. ``ranks`` and ``alphas`` are [n][S] (per-slice ranks of the
+    same slot may differ; 0 leaves the slot empty in that slice)."""
+    slot_ids = np.asarray(slot_ids, np.int32)
+    ranks = [np.asarray(r, np.int32) for r in ranks]
+    names = names or [f"slice{i}" for i in range(len(d_outs))]
+    own_pool = pool is None
+    pool = pool or ThreadPoolExecutor(8)
+    try:
+        first = _projection(seed, 0, names[0], T, d_in, d_outs[0], dtype, ranks[0], np.asarray(alphas[0], np.float64),
+                            pool=pool)
+        projs = [first]
+        for i in range(1, len(d_outs)):
+            projs.append(_projection(seed, i, names[i], T, d_in, d_outs[i], dtype, ranks[i],
+                                     np.asarray(alphas[i], np.float64), x=first.x, pool=pool))
+    finally:
+        if own_pool:
+            pool.shutdown()
+    rm = int(r_max if r_max is not None else max(1, max(int(r.max(initial=0)) for r in ranks)))
+    return Workload("slices", dtype, T, S, rm, slot_ids, projs)
+
+
+def make_qkv_decode(seed: int = 2, layer: int = 0, pool=None) -> Workload:
+    """The q/k/v projections of one Llama-3-8B attention layer at decode: the
+    slot structure of the q_proj decode workload (T=64, S=9, rank 16, alpha
+    32, 8 adapters x 8 tokens shuffled) with k and v of width d_kv = 1024."""
+    g = np.random.default_rng([seed, _TAG_SLOTS])
+    T, S, r = 64, 9, 16
+    slot_ids = g.permutation(np.repeat(np.arange(1, 9), 8)).astype(np.int32)
+    ranks = np.array([0] + [r] * (S - 1), np.int32)
+    alphas = np.array([0.0] + [32.0] * (S - 1))
+    wseed = seed if layer == 0 else seed * 1000003 + layer
+    return make_slices(wseed * 101 + 7, T, 4096, [4096, 1024, 1024], S, [ranks] * 3, [alphas] * 3, slot_ids,
+                       names=["q_proj", "k_proj", "v_proj"], pool=pool)

@@ -28,8 +28,10 @@ LORA_PLAN_ROWS = 16
 EXPORTS = (
     "lora_pool_create", "lora_pool_destroy", "lora_pool_install", "lora_pool_clear", "lora_pool_rank",
     "lora_plan", "lora_plan_max_items", "lora_workspace_bytes", "lora_linear", "lora_shrink",
-    "lora_status_string", "lora_profile_begin", "lora_profile_end",
+    "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_workspace_bytes_multi",
+    "lora_linear_multi",
 )
+LORA_MAX_SLICES = 4
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 _CODE = {"bf16": LORA_BF16, "f32": LORA_F32}
@@ -44,6 +46,11 @@ class LoraError(RuntimeError):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("S", ctypes.c_int32), ("T_a", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("n_items", ctypes.c_int32), ("max_seg", ctypes.c_int32)]
+
+
+class SliceDesc(ctypes.Structure):
+    """lora_slice: one projection of a multi-slice call."""
+    _fields_ = [("pool", ctypes.c_void_p), ("W", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class KernelStat(ctypes.Structure):
@@ -75,6 +82,10 @@ def lib():
             L.lora_workspace_bytes.argtypes = [_P, _I]
             L.lora_workspace_bytes.restype = _SZ
             L.lora_linear.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
+            L.lora_workspace_bytes_multi.argtypes = [ctypes.POINTER(SliceDesc), _I, _I]
+            L.lora_workspace_bytes_multi.restype = _SZ
+            L.lora_linear_multi.argtypes = [ctypes.POINTER(SliceDesc), _I, _P, _P, _P, _P, ctypes.POINTER(PlanInfo),
+                                            _P, _SZ, _P]
             L.lora_shrink.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
             L.lora_profile_begin.argtypes = [_I]
             L.lora_profile_end.argtypes = [ctypes.POINTER(KernelStat), _I, ctypes.POINTER(_I)]
@@ -274,6 +285,48 @@ def linear(x: torch.Tensor, W: torch.Tensor, pool: Pool, p: Plan, y: torch.Tenso
     _check(lib().lora_linear(pool.handle, x.data_ptr(), W.data_ptr(), to, ip, wk, ctypes.byref(p.info), y.data_ptr(),
                              ws.data_ptr(), ws.numel() * ws.element_size(), _stream(x.device)), "lora_linear")
     return y
+
+
+def _slice_array(pools, Ws=None, ys=None):
+    n = len(pools)
+    arr = (SliceDesc * max(n, 1))()
+    for i, pool in enumerate(pools):
+        arr[i].pool = pool.handle
+        arr[i].W = Ws[i].data_ptr() if Ws is not None else None
+        arr[i].y = ys[i].data_ptr() if ys is not None else None
+    return arr
+
+
+def workspace_bytes_multi(pools, T: int) -> int:
+    """lora_workspace_bytes_multi (0 when the pools cannot share a call)."""
+    return int(lib().lora_workspace_bytes_multi(_slice_array(pools, None, None), len(pools), int(T)))
+
+
+def linear_multi(x: torch.Tensor, Ws, pools, p: Plan, ys=None, workspace: torch.Tensor | None = None):
+    """lora_linear_multi: y_i = x W_i^T + per-row correction from pools[i],
+    for slices that share x and the plan (a merged q/k/v or gate/up)."""
+    n = len(pools)
+    if not 1 <= n <= LORA_MAX_SLICES or len(Ws) != n:
+        raise ValueError(f"need 1..{LORA_MAX_SLICES} pools and as many weights")
+    tdt = _TORCH_DTYPE[pools[0].dtype]
+    T = p.T
+    _dev_tensor(x, tdt, "x", (T, pools[0].d_in))
+    if p.dev is None:
+        raise ValueError("plan was not uploaded")
+    if ys is None:
+        ys = [torch.empty((T, pl.d_out), dtype=tdt, device=x.device) for pl in pools]
+    for i, pl in enumerate(pools):
+        _dev_tensor(Ws[i], tdt, f"W[{i}]", (pl.d_out, pl.d_in))
+        _dev_tensor(ys[i], tdt, f"y[{i}]", (T, pl.d_out))
+    arr = _slice_array(pools, Ws, ys)
+    if workspace is None:
+        need = int(lib().lora_workspace_bytes_multi(arr, n, T))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    to, ip, wk = p.dev_ptrs()
+    _check(lib().lora_linear_multi(arr, n, x.data_ptr(), to, ip, wk, ctypes.byref(p.info), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream(x.device)),
+           "lora_linear_multi")
+    return ys
 
 
 def shrink(x: torch.Tensor, pool: Pool, p: Plan, h: torch.Tensor | None = None) -> torch.Tensor:

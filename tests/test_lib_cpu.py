@@ -143,3 +143,19 @@ def test_host_argument_errors():
     assert L.lora_pool_clear(None, 1, None) == lora.LORA_EINVAL
     assert L.lora_pool_rank(None, 0) == -1
     assert L.lora_workspace_bytes(None, 10) == 0
+
+
+def test_multi_host_argument_errors():
+    """lora_linear_multi refuses a missing slice array, a slice count outside
+    [1, LORA_MAX_SLICES] and a slice without pool before touching the GPU."""
+    L = lora.lib()
+    info = lora.PlanInfo()
+    arr = (lora.SliceDesc * 5)()
+    assert L.lora_linear_multi(None, 1, 1, 1, 1, 1, ctypes.byref(info), 1, 0, None) == lora.LORA_EINVAL
+    for n in (0, -1, lora.LORA_MAX_SLICES + 1):
+        assert L.lora_linear_multi(arr, n, 1, 1, 1, 1, ctypes.byref(info), 1, 0, None) == lora.LORA_EINVAL
+    assert L.lora_linear_multi(arr, 1, 1, 1, 1, 1, ctypes.byref(info), 1, 0, None) == lora.LORA_EINVAL
+    assert L.lora_workspace_bytes_multi(None, 1, 10) == 0
+    assert L.lora_workspace_bytes_multi(arr, 2, 10) == 0
+    with pytest.raises(ValueError):
+        lora.linear_multi(None, [], [], None)
