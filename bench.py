@@ -216,7 +216,7 @@ def main():
     k1_bytes = 2 * T * d_in + 2 * d_in * d_out + a_bytes
     k1_gbs = k1_bytes / (t1 * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("splitk_gemm_kernel<8>"),
+            "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("splitk_gemm_kernel<8, false>"),
             "kernel": "splitk_gemm_kernel (base GEMM K-split partials + SGMV shrink workgroups)",
             "bytes_per_launch": k1_bytes, "mean_us": round(t1, 3)}
     call_bytes = sb["base"] + sb["shrink"] + sb["expand"]
