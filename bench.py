@@ -13,10 +13,13 @@ value = T * layers / step time: tokens through one adapted linear per second
 
 After the timed region the same step runs eagerly with the library's
 per-kernel HIP-event timing on (behind a long filler GEMM so the host stays
-ahead of the GPU); those durations give the roofline figures. Then the
-prefill-shaped gate projection (T = 8192, 4096 -> 14336) is timed the same
-way for the base GEMM's matrix-core fraction, and the fp64 CPU oracle is
-timed on a bounded sample of the decode workload.
+ahead of the GPU); those durations give the roofline figures. Then, each as
+its own labelled figure: a warm call (one layer repeated, MALL-resident) and
+the launch floor of a replayed graph; q/k/v in one lora_linear_multi call
+against three calls; the prefill-shaped gate projection (T = 8192,
+4096 -> 14336) for the base GEMM's matrix-core fraction; single cold calls
+of the k/v mixed-rank and o/down workloads; and the fp64 CPU oracle on a
+bounded sample of the decode workload.
 
 Prints one JSON line. --gpus N > 1 is refused: this build runs on one GPU.
 """
@@ -52,6 +55,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-slices", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 256 MiB device copies (reference for the FETCH_SIZE/WRITE_SIZE counters)")
@@ -228,9 +232,51 @@ def main():
             "call_us": round(t1 + t2, 3),
             "call_achieved_gbs": round(call_bytes / ((t1 + t2) * 1e-6) / 1e9, 1),
             "call_frac_hbm": round(call_bytes / ((t1 + t2) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    kernels = {k: {"mean_us": round(v["mean_ms"] * 1e3, 3), "min_us": round(v["min_ms"] * 1e3, 3),
-                   "count": v["count"]} for k, v in stats.items()}
+    kernels = {k: {"mean_us": round(v["mean_ms"] * 1e3, 3), "median_us": round(v["median_ms"] * 1e3, 3),
+                   "min_us": round(v["min_ms"] * 1e3, 3), "count": v["count"]} for k, v in stats.items()}
     log(f"kernels: {kernels}; base-only: {stats_base}")
+
+    # ---- warm figure and launch floor -------------------------------------------
+    # warm: layer 0 called 32 times (its 32 MB W stays in the 256 MB MALL);
+    # floor: 32 one-element fill kernels, graph-replayed the same way
+    def graph_us(fn, n_calls, reps=20):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * n_calls)
+
+    def warm_calls():
+        for _ in range(L):
+            lora.linear(xs[0], Ws[0], pools[0], p, y=ys[0], workspace=ws)
+
+    tiny = torch.zeros(1, device="cuda")
+
+    def tiny_fills():
+        for _ in range(L):
+            tiny.fill_(1.0)
+
+    warm_us = graph_us(warm_calls, L)
+    floor_us = graph_us(tiny_fills, L)
+    warm = {"call_us": round(warm_us, 3), "tokens_per_s": round(T / (warm_us * 1e-6), 1),
+            "note": "one layer's weights called 32 times in a graph (MALL-resident)"}
+    floor = {"kernel_us": round(floor_us, 3),
+             "note": "one-element fill kernel, 32 per graph: launch-to-launch floor of a replayed step"}
+    log(f"warm: {warm}; floor: {floor}")
 
     # ---- q/k/v in one call against three calls ----------------------------------
     slices = None
@@ -344,6 +390,49 @@ def main():
                    "kernels": {k: round(v["mean_ms"] * 1e3, 2) for k, v in s3.items()}}
         log(f"prefill: {prefill}")
 
+    # ---- other configs, single cold calls ------------------------------------------
+    others = None
+    if not args.no_configs:
+        torch.cuda.empty_cache()
+        flush = torch.empty(512 * 2**20, dtype=torch.uint8, device="cuda")
+        others = {}
+        for cfg in (4, 5):
+            wc = make_config(cfg)
+            pc = lora.plan(wc.slot_ids, wc.S)
+            for pr in wc.projections:
+                pool_c = lora.Pool(wc.S, wc.r_max, pr.d_in, pr.d_out, "bf16")
+                for s_, a in sorted(pr.adapters.items()):
+                    pool_c.install(s_, lora.to_device(a.A, "bf16"), lora.to_device(a.B, "bf16"), a.alpha)
+                xc, Wc = lora.to_device(pr.x, "bf16"), lora.to_device(pr.W, "bf16")
+                yc = torch.empty((wc.T, pr.d_out), dtype=torch.bfloat16, device="cuda")
+                lora.linear(xc, Wc, pool_c, pc, y=yc)
+                torch.cuda.synchronize()
+                n_c = 10
+                lora.profile_begin(8 * n_c + 64)
+                for _ in range(n_c):
+                    flush.add_(1)  # evict the MALL and L2 before each call
+                    lora.linear(xc, Wc, pool_c, pc, y=yc)
+                sc = lora.profile_end()
+                torch.cuda.synchronize()
+                call_us = sum(v["median_ms"] for v in sc.values()) * 1e3
+                entry = {"T": wc.T, "d_in": pr.d_in, "d_out": pr.d_out, "S": wc.S,
+                         "call_us": round(call_us, 2), "tokens_per_s": round(wc.T / (call_us * 1e-6), 1),
+                         "kernels_median_us": {k: round(v["median_ms"] * 1e3, 2) for k, v in sc.items()}}
+                rk = wc.ranks
+                if "gemm_splitk" in sc:
+                    a_b = sum(2 * int(rk[s_]) * pr.d_in for s_ in acc.segments(wc.slot_ids, rk))
+                    kb = 2 * wc.T * pr.d_in + 2 * pr.d_in * pr.d_out + a_b
+                    gbs = kb / (sc["gemm_splitk"]["median_ms"] * 1e-3) / 1e9
+                    entry["kernel1_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+                else:
+                    fl = acc.base_flops(wc.T, pr.d_in, pr.d_out)
+                    tf = fl / (sc["gemm_bf16"]["median_ms"] * 1e-3) / 1e12
+                    entry["gemm_frac_mfma"] = round(tf / BF16_PEAK_TFLOPS, 4)
+                others[f"config{cfg} {pr.name}"] = entry
+                del pool_c, xc, Wc, yc
+        del flush
+        log(f"other configs: {others}")
+
     if args.copy_calibration:
         src = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -377,7 +466,8 @@ def main():
                    "T": T, "d_in": d_in, "d_out": d_out, "S": S, "rank": 16, "layers": L,
                    "mode": "eager" if graph is None else "hip graph replay"},
         "roofline": roof, "cpu_baseline": cpu,
-        "correction": corr, "kernels": kernels, "prefill": prefill, "slices": slices,
+        "correction": corr, "kernels": kernels, "warm": warm, "launch_floor": floor, "prefill": prefill,
+        "slices": slices, "other_configs": others,
     }
     print(json.dumps(out), flush=True)
 

@@ -223,20 +223,21 @@ int lora_shrink(const lora_pool* pool, const void* x, const int32_t* token_order
 
 /*
  * Per-kernel timing, for diagnostics and the benchmark's roofline figures.
- * Between lora_profile_begin and lora_profile_end, lora_linear and
- * lora_shrink record a HIP event pair around every kernel they launch, on
- * the stream it is launched on (not while that stream is being captured
- * into a graph, and at most max_records kernels). lora_profile_end waits for
- * the recorded events and writes one entry per kernel name, in first-launch
- * order, into out[0..cap); *n_out receives the number of names. Profiling
- * serialises lora_linear calls across threads while it is on.
+ * Between lora_profile_begin and lora_profile_end, lora_linear,
+ * lora_linear_multi and lora_shrink record a HIP event pair around every
+ * kernel they launch, on the stream it is launched on (not while that stream
+ * is being captured into a graph, and at most max_records kernels).
+ * lora_profile_end waits for the recorded events and writes one entry per
+ * kernel name, in first-launch order, into out[0..cap): count, mean, min,
+ * max and median duration; *n_out receives the number of names. Profiling
+ * serialises the calls across threads while it is on.
  * Errors: LORA_EINVAL (begin while on, end while off, max_records < 8),
  * LORA_ESPACE (more names than cap), LORA_EHIP.
  */
 typedef struct lora_kernel_stat {
     char name[48];
     int32_t count;
-    double mean_ms, min_ms, max_ms;
+    double mean_ms, min_ms, max_ms, median_ms;
 } lora_kernel_stat;
 
 int lora_profile_begin(int max_records);

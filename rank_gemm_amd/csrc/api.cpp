@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <new>
@@ -385,6 +386,7 @@ int lora_profile_end(lora_kernel_stat* out, int cap, int* n_out) {
     struct Acc {
         int n = 0;
         double sum = 0, mn = 1e30, mx = 0;
+        std::vector<float> all;
     };
     std::map<std::string, Acc> acc;
     std::vector<std::string> order;
@@ -405,6 +407,7 @@ int lora_profile_end(lora_kernel_stat* out, int cap, int* n_out) {
         a.sum += ms;
         a.mn = ms < a.mn ? ms : a.mn;
         a.mx = ms > a.mx ? ms : a.mx;
+        a.all.push_back(ms);
     }
     for (auto& r : p.recs) {
         p.spare.push_back(r.a);
@@ -414,13 +417,19 @@ int lora_profile_end(lora_kernel_stat* out, int cap, int* n_out) {
     int n = 0;
     for (const auto& name : order) {
         if (out && n < cap) {
-            const Acc& a = acc[name];
+            Acc& a = acc[name];
             std::memset(&out[n], 0, sizeof(out[n]));
             std::strncpy(out[n].name, name.c_str(), sizeof(out[n].name) - 1);
             out[n].count = a.n;
             out[n].mean_ms = a.sum / a.n;
             out[n].min_ms = a.mn;
             out[n].max_ms = a.mx;
+            // median: the middle element, or the mean of the two middle ones
+            const size_t h = a.all.size() / 2;
+            std::nth_element(a.all.begin(), a.all.begin() + h, a.all.end());
+            double med = a.all[h];
+            if (a.all.size() % 2 == 0) med = 0.5 * (med + *std::max_element(a.all.begin(), a.all.begin() + h));
+            out[n].median_ms = med;
         }
         ++n;
     }

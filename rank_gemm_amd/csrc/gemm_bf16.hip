@@ -14,10 +14,11 @@
 // equal those of a run with no adapter row.
 //
 // Two paths, chosen by (T, d_out) only:
-//  * tiled (prefill-sized T, this file): 256 x 256 macro tiles over 8 waves
-//    with K in stages of 32 through a 3-deep LDS ring filled by direct-to-LDS
-//    loads (128 x 128 and 64 x 128 tiles with 4 waves and register-staged
-//    loads for smaller T); the shrink runs before it as its own kernel.
+//  * tiled (T above decode sizes, this file): one kernel template with K in
+//    stages of 64 through an LDS ring filled by direct-to-LDS loads; the
+//    macro tile is the largest of 256 x 256, 256 x 128, 128 x 128 (8 waves)
+//    and 64 x 128 (4 waves) that still gives most CUs a tile. The shrink runs
+//    before it as its own kernel.
 //  * split-K (decode-sized T, splitk.hip): a K-split GEMM with the shrink in
 //    extra workgroups of the same launch, then a kernel that adds the splits
 //    and applies the expand.
@@ -27,171 +28,104 @@
 
 namespace lora {
 
-// ------------------------------------------------------------------ tiled --
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_tiled_kernel(const uint16_t* __restrict__ X,
-                                                                 const uint16_t* __restrict__ W,
-                                                                 uint16_t* __restrict__ Y, int M, int N, int K,
-                                                                 int tiles_m, int tiles_n, Fuse f) {
-    constexpr int WTM = BM / 2, WTN = BN / 2;
-    constexpr int FM = WTM / 16, FN = WTN / 16;
-    constexpr int AC = BM * 8 / kThreads;  // 16-byte chunks per thread per stage
-    constexpr int BC = BN * 8 / kThreads;
-    __shared__ u32x4 lds[2 * (BM + BN) * 8];
-    __shared__ SlotMeta meta;
-    u32x4* As = lds;
-    u32x4* Bs = lds + 2 * BM * 8;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const MetaView mv = stage_meta(f, &meta);  // ordered by the main loop's barriers
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = (K + kBK - 1) / kBK;
-
-    const int lc = tid & 7, lr = tid >> 3;
-    const uint16_t* xrow[AC];  // gathered x rows of this thread's chunks (clamped; xok masks)
-    bool xok[AC];
-#pragma unroll
-    for (int i = 0; i < AC; ++i) {
-        const int p = m0 + lr + 32 * i;
-        xok[i] = p < M;
-        xrow[i] = X + (int64_t)f.token_order[min(p, M - 1)] * K;
-    }
-    const int mend = min(M, m0 + BM);
-    // interior tiles (the uniform common case) load without masks; elsewhere
-    // a masked-off chunk reads zeros (or_zero selects the address)
-    const bool interior = m0 + BM <= M && n0 + BN <= N && (K % kBK) == 0;
-    const uint16_t* wtile = W + (int64_t)n0 * K;
-    u32x4 ra[AC], rb[BC];
-    auto gload = [&](int it) {
-        if (it < nk) {
-            const int kk = it * kBK + lc * 8;
-            if (interior) {
-#pragma unroll
-                for (int i = 0; i < AC; ++i) ra[i] = *(const u32x4*)(xrow[i] + kk);
-#pragma unroll
-                for (int i = 0; i < BC; ++i) rb[i] = *(const u32x4*)(wtile + (int64_t)(lr + 32 * i) * K + kk);
-                return;
-            }
-            const bool kin = kk < K;  // K % 8 == 0: a chunk is fully in or out
-#pragma unroll
-            for (int i = 0; i < AC; ++i) ra[i] = *or_zero(kin && xok[i], xrow[i] + kk);
-#pragma unroll
-            for (int i = 0; i < BC; ++i) {
-                const int r = n0 + lr + 32 * i;
-                rb[i] = *or_zero(kin && r < N, W + (int64_t)r * K + kk);
-            }
-            return;
-        }
-        ExtraStep x{};
-        extra_steps(mv, f, m0, mend, it - nk, &x);
-        const int k0 = x.t * 64 + lc * 8;       // position in the 2 rp extension
-        const int q0 = k0 < f.rp ? k0 : k0 - f.rp;  // rank of the chunk (rp % 8 == 0)
-        const bool qin = k0 < 2 * f.rp && q0 < x.r;
-#pragma unroll
-        for (int i = 0; i < AC; ++i) {
-            const int p = m0 + lr + 32 * i;
-            ra[i] = *or_zero(qin && p >= x.sb && p < x.se, f.ext + (int64_t)p * 2 * f.rp + k0);
-        }
-#pragma unroll
-        for (int i = 0; i < BC; ++i) {
-            const int n = n0 + lr + 32 * i;
-            rb[i] = *or_zero(qin && n < N, f.B_pool + ((int64_t)x.s * N + n) * f.r_max + q0);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < AC; ++i) As[buf * BM * 8 + swz(lr + 32 * i, lc)] = ra[i];
-#pragma unroll
-        for (int i = 0; i < BC; ++i) Bs[buf * BN * 8 + swz(lr + 32 * i, lc)] = rb[i];
-    };
-
-    f32x4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    // the slot metadata is in LDS now: count the expand's extra K steps
-    const int nt = nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr) : 0);
-    for (int kt = 0; kt < nt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nt) gload(kt + 1);
-        const u32x4* Ab = As + buf * BM * 8;
-        const u32x4* Bb = Bs + buf * BN * 8;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c = kk * 4 + (lane >> 4);
-            u32x4 af[FM], bfg[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = Ab[swz(wm * WTM + i * 16 + (lane & 15), c)];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bfg[j] = Bb[swz(wn * WTN + j * 16 + (lane & 15), c)];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(af[i], bfg[j], acc[i][j]);
-        }
-        if (kt + 1 < nt) sstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    const int p0 = m0 + wm * WTM, nb = n0 + wn * WTN;
-    if (!f.ext) fused_expand<FM, FN>(acc, f, mv, p0, nb, M, N, lane);
-    store_tile<FM, FN>(acc, Y, f.token_order, p0, nb, M, N, lane);
+// --------------------------------------------- tiled, direct-to-LDS loads --
+// BM x BN macro tiles over WM x WN waves, wave tile (BM / WM) x (BN / WN) of
+// 16 x 16 MFMA tiles; K in stages of BK (32 or 64) through NS LDS buffers,
+// filled by direct-to-LDS loads (global_load_lds_dwordx4: 16 B per lane,
+// written at the wave's LDS base + 16 * lane). A row of a stage is CPR = BK / 8
+// chunks of 16 B; one load instruction covers 64 / CPR rows. Lane i fetches
+// row i / CPR, chunk (i % CPR) ^ swizzle(row): the bank swizzle is applied by
+// choosing the source, so the MFMA fragment reads (row l % 16, chunk l / 16 of
+// a 32-k half) are free of bank conflicts. With BK = 64 each row piece is a
+// whole 128-byte line, so a stage costs half as many memory requests per byte
+// as with BK = 32. Stage kt + NS - 1 is loaded once every wave is past stage
+// kt's barrier. The fragment reads are issued and waited on by hand: with LDS
+// loads in flight the compiler would wait for all of them at the first use.
+template <int CPR>
+__device__ __forceinline__ int row_swz(int r) {
+    if constexpr (CPR == 8) return r & 7;
+    else return ((r >> 1) ^ (r >> 2)) & 3;
 }
 
-// ------------------------------------------------------- tiled, 256 x 256 --
-// 8 waves (2 per SIMD) as 2 x 4, wave tile 128 x 64 (8 x 4 MFMA tiles); K in
-// stages of 32 through kDmaStages LDS buffers, filled by direct-to-LDS loads
-// (global_load_lds_dwordx4: 16 B per lane, written at the wave's LDS base +
-// 16 * lane). A stage's A and B operands are 16 blocks each of 16 rows x 32 k
-// (1 KB). Lane i of a block load fetches row i / 4, k chunk (i % 4) ^
-// dma_swz(row): the bank swizzle is applied by choosing the source, so the
-// MFMA fragment reads (row l % 16, chunk l / 16) are free of bank conflicts.
-// Stage kt + kDmaStages - 1 is loaded once every wave is past stage kt's
-// barrier. The fragment reads are issued and waited on by hand: with LDS
-// loads in flight the compiler would wait for all of them at the first use.
-constexpr int kDmaStages = 3;
-constexpr int kDmaStageChunks = (256 + 256) * 32 * 2 / 16;  // 16-byte chunks
-
-__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// fragment I.. of N, read from consecutive fragment slots (STRIDE bytes apart) at `base`
+template <int I, int N, int STRIDE>
+__device__ __forceinline__ void read_frags(u32x4 (&fr)[N], uint32_t base) {
+    if constexpr (I < N) {
+        fr[I] = lds_read16<I * STRIDE>(base);
+        read_frags<I + 1, N, STRIDE>(fr, base);
+    }
+}
+template <int N, int I, int FJ>
+__device__ __forceinline__ void tie_frags(u32x4 (&fr)[FJ]) {
+    if constexpr (I < FJ) {
+        lds_landed<N>(fr[I]);
+        tie_frags<N, I + 1, FJ>(fr);
+    }
+}
+// MFMA rows I.. of the wave tile; row i waits for A fragment i only (the B
+// fragments and A fragment 0 were waited on before row 0)
+template <int I, int FI, int FJ>
+__device__ __forceinline__ void mfma_rows(f32x4 (&acc)[FI][FJ], u32x4 (&af)[FI], const u32x4 (&bf)[FJ]) {
+    if constexpr (I < FI) {
+        if constexpr (I > 0) lds_landed<FI - 1 - I>(af[I]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[I][j] = mfma16x16x32(af[I], bf[j], acc[I][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows<I + 1, FI, FJ>(acc, af, bf);
+    }
+}
+// stage kt landed: at most `ahead` later stages (DPW loads each) in flight
+template <int A, int DPW>
+__device__ __forceinline__ void wait_stage(int ahead) {
+    if constexpr (A <= 0) {
+        vm_landed<0>();
+    } else {
+        if (ahead >= A) vm_landed<A * DPW>();
+        else wait_stage<A - 1, DPW>(ahead);
+    }
+}
 
 // EPI: the expand runs in the epilogue from fp32 h (r_max % 8 != 0);
 // otherwise it runs as extra K steps (or there is no adapter row).
-// KTAIL: K % 32 != 0, the last base stage masks the chunks past K.
-template <bool EPI, bool KTAIL>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_dma_kernel(
+// KTAIL: K % BK != 0, the last base stage masks the chunks past K.
+template <int BM, int BN, int WM, int WN, int BK, int NS, bool EPI, bool KTAIL>
+__global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4))) void gemm_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, Fuse f) {
-    constexpr int BM = 256, BN = 256, BK = 32, NS = kDmaStages, STAGE = kDmaStageChunks;
+    constexpr int NW = WM * WN, CPR = BK / 8, RPI = 64 / CPR;  // chunks per row, rows per load instruction
+    constexpr int FI = BM / WM / 16, FJ = BN / WN / 16;        // MFMA tiles of a wave
+    constexpr int DA = BM / RPI / NW, DB = BN / RPI / NW;      // load instructions of a wave per stage
+    constexpr int DPW = DA + DB, STAGE = (BM + BN) * CPR;      // stage size in 16-byte chunks
+    constexpr int FSTRIDE = 16 * CPR * 16;                     // bytes between 16-row fragments
+    static_assert(BK == 32 || BK == 64, "stage depth");
+    static_assert(DA * NW * RPI == BM && DB * NW * RPI == BN, "load instructions per wave");
+    static_assert(FI <= 16 && NS >= 2 && (NS - 2) * DPW < 64, "wait counters");
     __shared__ u32x4 lds[NS * STAGE];
     __shared__ SlotMeta meta;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WN, wn = wave % WN;
     const MetaView mv = stage_meta(f, &meta);
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int mend = min(M, m0 + BM);
     const int nk = (K + BK - 1) / BK;
-    // this lane's rows of the two A and two B blocks it loads (rows past M or
-    // N are clamped: their products land in outputs that are not stored)
-    const int rl = lane >> 2;
-    const int cl = (lane & 3) ^ dma_swz(rl);
-    int prow[2], ncol[2];
-    const uint16_t* ap[2];
-    const uint16_t* bp[2];
+    // this lane's rows of the A and B pieces it loads (rows past M or N are
+    // clamped: their products land in outputs that are not stored)
+    const int rl = lane / CPR;
+    const int cl = (lane % CPR) ^ row_swz<CPR>(rl);
+    int prow[DA], ncol[DB];
+    const uint16_t* ap[DA];
+    const uint16_t* bp[DB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        prow[b] = m0 + (wave * 2 + b) * 16 + rl;
-        ncol[b] = n0 + (wave * 2 + b) * 16 + rl;
+    for (int b = 0; b < DA; ++b) {
+        prow[b] = m0 + (wave * DA + b) * RPI + rl;
         ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + cl * 8;
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+        ncol[b] = n0 + (wave * DB + b) * RPI + rl;
         bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
     }
     __syncthreads();  // slot metadata staged
@@ -200,110 +134,123 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int nt = __builtin_amdgcn_readfirstlane(
         nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0));
 
-    auto issue = [&](int kt) {
-        u32x4* st = lds + (kt % NS) * STAGE;
-        gptr<u32x4> asrc[2], bsrc[2];
-        if (kt < nk) {
-            const int k = kt * BK;
-            const bool kin = !KTAIL || k + cl * 8 < K;  // K % 8 == 0: a chunk is fully in or out
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                asrc[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
-                bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
+    // the expand's extra steps come first: their operands (B_s rows, scaled
+    // h) are cold, and the base stages that follow hide their latency
+    const int ne = nt - nk;
+    // Cursor over the extra steps (slot, its segment, rank, step within the
+    // slot), advanced once per extra stage issued. The slot metadata is read
+    // from its LDS copy (the host takes this path only for pools of at most
+    // kMetaSlots slots): a flat or global load here would also wait for every
+    // direct-to-LDS load in flight.
+    auto md_indptr = [&](int i) { return meta.indptr[i]; };
+    auto md_rank = [&](int i) { return meta.rank[i]; };
+    const int spk = (2 * f.rp + BK - 1) / BK;  // extra steps per slot
+    int cs = f.S, csb = 0, cse = 0, cr = 0, ct = 0;
+    auto seek = [&](int s) {  // first slot >= s whose segment meets the tile, with a nonzero rank
+        for (; s < f.S; ++s) {
+            const int sb = md_indptr(s), se = md_indptr(s + 1);
+            if (sb >= mend) {
+                s = f.S;
+                break;
             }
-        } else {
-            ExtraStep x{};
-            extra_steps(mv, f, m0, mend, kt - nk, &x, BK);
-            const int k = x.t * BK + cl * 8;            // position in the 2 rp extension
-            const int q = k < f.rp ? k : k - f.rp;      // rank of the chunk (rp % 8 == 0)
-            const bool qin = k < 2 * f.rp && q < x.r;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                asrc[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
-                bsrc[b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+            const int r = md_rank(s);
+            if (s != 0 && r != 0 && se > m0 && se > sb) {
+                csb = sb;
+                cse = se;
+                cr = r;
+                break;
             }
         }
+        cs = s;
+        ct = 0;
+    };
+    if (ne > 0) {
+        int lo = 0, hi = f.S - 1;  // last slot whose segment starts at or before m0
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (md_indptr(mid) <= m0) lo = mid;
+            else hi = mid - 1;
+        }
+        seek(lo);
+    }
+    auto issue = [&](int kt) {
+        u32x4* st = lds + (kt % NS) * STAGE;
+        gptr<u32x4> asrc[DA], bsrc[DB];
+        if (kt >= ne) {
+            const int k = (kt - ne) * BK;
+            const bool kin = !KTAIL || k + cl * 8 < K;  // K % 8 == 0: a chunk is fully in or out
 #pragma unroll
-        for (int b = 0; b < 2; ++b) dma16(asrc[b], st + (wave * 2 + b) * 64);
+            for (int b = 0; b < DA; ++b) asrc[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) dma16(bsrc[b], st + 16 * 64 + (wave * 2 + b) * 64);
+            for (int b = 0; b < DB; ++b) bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
+        } else {
+            const ExtraStep x{cs, csb, cse, cr, ct};
+            if (++ct == spk) seek(cs + 1);
+            const int k = x.t * BK + cl * 8;        // position in the 2 rp extension
+            const int q = k < f.rp ? k : k - f.rp;  // rank of the chunk (rp % 8 == 0)
+            const bool qin = k < 2 * f.rp && q < x.r;
+#pragma unroll
+            for (int b = 0; b < DA; ++b)
+                asrc[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+                bsrc[b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+        }
+#pragma unroll
+        for (int b = 0; b < DA; ++b) dma16(asrc[b], st + (wave * DA + b) * 64);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) dma16(bsrc[b], st + BM * CPR + (wave * DB + b) * 64);
     };
 
-    f32x4 acc[8][4];
+    f32x4 acc[FI][FJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int fr = lane & 15, fc = lane >> 4;
-    const int foff = fr * 4 + (fc ^ dma_swz(fr));
-    const uint32_t abase = lds_offset(lds + wm * 8 * 64 + foff);
-    const uint32_t bbase = lds_offset(lds + 16 * 64 + wn * 4 * 64 + foff);
+    uint32_t abase[BK / 32], bbase[BK / 32];  // per 32-k half of a stage
+#pragma unroll
+    for (int h = 0; h < BK / 32; ++h) {
+        const int foff = fr * CPR + ((h * 4 + fc) ^ row_swz<CPR>(fr));
+        abase[h] = lds_offset(lds + wm * FI * 16 * CPR + foff);
+        bbase[h] = lds_offset(lds + BM * CPR + wn * FJ * 16 * CPR + foff);
+    }
 
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
         if (s < nt) issue(s);
     for (int kt = 0; kt < nt; ++kt) {
-        // stage kt landed for this wave (the one issued after it may be in flight)
-        static_assert(NS == 3, "wait counts assume 3 stages");
-        if (kt + 1 < nt) vm_landed<4>();
-        else vm_landed<0>();
+        // stage kt landed for this wave (the ones issued after it may be in flight)
+        wait_stage<NS - 2, DPW>(nt - 1 - kt);
         stage_barrier();
         if (kt + NS - 1 < nt) issue(kt + NS - 1);  // into stage kt - 1's buffer
         const uint32_t so = (kt % NS) * STAGE * 16;
-        u32x4 bf[4], af[8];
-        bf[0] = lds_read16<0>(bbase + so);
-        bf[1] = lds_read16<1024>(bbase + so);
-        bf[2] = lds_read16<2048>(bbase + so);
-        bf[3] = lds_read16<3072>(bbase + so);
-        af[0] = lds_read16<0>(abase + so);
-        af[1] = lds_read16<1024>(abase + so);
-        af[2] = lds_read16<2048>(abase + so);
-        af[3] = lds_read16<3072>(abase + so);
-        af[4] = lds_read16<4096>(abase + so);
-        af[5] = lds_read16<5120>(abase + so);
-        af[6] = lds_read16<6144>(abase + so);
-        af[7] = lds_read16<7168>(abase + so);
-        lds_landed<7>(bf[0], af[0]);
-        lds_landed<7>(bf[1], bf[2]);
-        lds_landed<7>(bf[3]);
-        auto row = [&](auto i_) {
-            constexpr int i = decltype(i_)::value;
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        row(std::integral_constant<int, 0>{});
-        lds_landed<6>(af[1]);
-        row(std::integral_constant<int, 1>{});
-        lds_landed<5>(af[2]);
-        row(std::integral_constant<int, 2>{});
-        lds_landed<4>(af[3]);
-        row(std::integral_constant<int, 3>{});
-        lds_landed<3>(af[4]);
-        row(std::integral_constant<int, 4>{});
-        lds_landed<2>(af[5]);
-        row(std::integral_constant<int, 5>{});
-        lds_landed<1>(af[6]);
-        row(std::integral_constant<int, 6>{});
-        lds_landed<0>(af[7]);
-        row(std::integral_constant<int, 7>{});
+        for (int h = 0; h < BK / 32; ++h) {
+            u32x4 bf[FJ], af[FI];
+            read_frags<0, FJ, FSTRIDE>(bf, bbase[h] + so);
+            read_frags<0, FI, FSTRIDE>(af, abase[h] + so);
+            tie_frags<FI - 1, 0, FJ>(bf);
+            lds_landed<FI - 1>(af[0]);
+            mfma_rows<0, FI, FJ>(acc, af, bf);
+        }
     }
-    const int p0 = m0 + wm * 128, nb = n0 + wn * 64;
-    if constexpr (EPI) fused_expand<8, 4>(acc, f, mv, p0, nb, M, N, lane);
-    store_tile<8, 4>(acc, Y, f.token_order, p0, nb, M, N, lane);
+    const int p0 = m0 + wm * FI * 16, nb = n0 + wn * FJ * 16;
+    if constexpr (EPI) fused_expand<FI, FJ>(acc, f, mv, p0, nb, M, N, lane);
+    store_tile<FI, FJ>(acc, Y, f.token_order, p0, nb, M, N, lane);
 }
 
 // ------------------------------------------------------------------ plan --
 GemmPlan gemm_bf16_plan(int M, int N, int K) {
     GemmPlan g{};
     if (M <= 0 || N <= 0 || K <= 0) return g;  // nothing to launch
-    const int64_t t256 = (int64_t)cdiv(M, 256) * cdiv(N, 256);
-    const int64_t t128 = (int64_t)cdiv(M, 128) * cdiv(N, 128);
-    const int64_t t64 = (int64_t)cdiv(M, 64) * cdiv(N, 128);
-    if (t256 >= 256) { g.bm = 256; g.bn = 256; return g; }
-    if (t128 >= 256) { g.bm = 128; g.bn = 128; return g; }
-    if (M > 256 && t64 >= 128) { g.bm = 64; g.bn = 128; return g; }
+    // the largest macro tile that still gives most of the 256 CUs a tile
+    auto n_tiles = [&](int bm, int bn) { return (int64_t)cdiv(M, bm) * cdiv(N, bn); };
+    constexpr int64_t kFill = 200;
+    if (n_tiles(256, 256) >= kFill) { g.bm = 256; g.bn = 256; return g; }
+    if (n_tiles(256, 128) >= kFill) { g.bm = 256; g.bn = 128; return g; }
+    if (n_tiles(128, 128) >= kFill) { g.bm = 128; g.bn = 128; return g; }
+    if (M > 256 && n_tiles(64, 128) >= 128) { g.bm = 64; g.bn = 128; return g; }
     // split-K: 64 x 64 tiles, enough K splits for ~256 workgroups
     g.bm = 64; g.bn = 64;
     g.n_mt = cdiv(M, 64);
@@ -327,6 +274,14 @@ static size_t split_workspace(int M, int n_nt_total, const GemmPlan& g, int n_sl
     const size_t py = (size_t)g.ks * g.n_mt * n_nt_total * 16 * 64 * 16;
     const size_t ph = (size_t)n_slices * g.hs * M * r_max * sizeof(float);
     return ((py + 255) & ~size_t(255)) + ((ph + 255) & ~size_t(255));
+}
+
+// tiled path: fp32 h [M][r_max] or bf16 hi / lo [M][2][round_up(r_max, 8)],
+// then the K-split shrink's planes (at most kShrinkSplitMaxBlocks x 16 rows)
+static size_t tiled_workspace(int M, int r_max) {
+    const size_t h_final = (size_t)M * ((r_max + 7) & ~7) * sizeof(float);
+    const size_t planes = (size_t)kShrinkSplitMaxBlocks * 16 * r_max * sizeof(float);
+    return ((h_final + 255) & ~size_t(255)) + planes;
 }
 
 static int total_tiles_n(const int* N, int n_slices) {
@@ -359,20 +314,23 @@ size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max) 
     for (int i = 0; i < n_slices; ++i) {
         if (N[i] <= 0) continue;
         const GemmPlan g = gemm_bf16_plan(M, N[i], K);
-        // fp32 h [M][r_max], or bf16 hi / lo [M][2][round_up(r_max, 8)]
-        const size_t h_final = (size_t)M * ((r_max + 7) & ~7) * sizeof(float);
-        const size_t b = g.nsub == 0 ? ((h_final + 255) & ~size_t(255)) : split_workspace(M, g.n_nt, g, 1, r_max);
+        const size_t b = g.nsub == 0 ? tiled_workspace(M, r_max) : split_workspace(M, g.n_nt, g, 1, r_max);
         need = b > need ? b : need;
     }
     return need;
 }
 
-template <int BM, int BN>
-static hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K,
-                               const Fuse& f, hipStream_t st, StageTimer* tm) {
+template <int BM, int BN, int WM, int WN, int BK, int NS>
+static hipError_t launch_dma(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
+                             bool epi, hipStream_t st, StageTimer* tm) {
     const int tiles_m = cdiv(M, BM), tiles_n = cdiv(N, BN);
-    return launch(tm, "gemm_bf16", gemm_tiled_kernel<BM, BN>, dim3(tiles_m * tiles_n), dim3(kThreads), st, X, W, Y,
-                  M, N, K, tiles_m, tiles_n, f);
+    const bool ktail = K % BK != 0;
+    auto ker = epi ? (ktail ? gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, true>
+                            : gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, false>)
+                   : (ktail ? gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, true>
+                            : gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, false>);
+    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(64 * WM * WN), st, X, W, Y, M, N, K, tiles_m,
+                  tiles_n, f);
 }
 
 // One slice on the tiled path: the shrink to final h, then the tiled GEMM
@@ -385,24 +343,32 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
            nullptr, (L.r_max + 7) & ~7};
     char* ws = static_cast<char*>(L.workspace);
     float* hbuf = reinterpret_cast<float*>(ws);
-    uint16_t* ext = (L.r_max % 8 == 0) ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+    // the expand as extra K steps needs r_max % 8 == 0 and the slot metadata in LDS
+    uint16_t* ext = (L.r_max % 8 == 0 && L.S <= kMetaSlots) ? reinterpret_cast<uint16_t*>(ws) : nullptr;
     f.h = ext ? nullptr : hbuf;
     f.ext = ext;
     if (L.adapters) {
-        const hipError_t e = sgmv_shrink(1, L.X, sl.A_pool, sl.rank, L.token_order, L.work, L.n_items,
-                                         ext ? nullptr : hbuf, K, L.r_max, st, tm, sl.scale, ext);
+        // few items over a long K: split K over more workgroups, then add the splits
+        int hs = 1, hkc = K;
+        if (L.n_items < kShrinkSplitMaxBlocks / 2) {
+            hs = min(8, kShrinkSplitMaxBlocks / max(L.n_items, 1));
+            hkc = max(256, (cdiv(K, hs) + 31) / 32 * 32);
+            hs = cdiv(K, hkc);
+        }
+        const size_t h_final = (size_t)M * ((L.r_max + 7) & ~7) * sizeof(float);
+        float* part = reinterpret_cast<float*>(ws + ((h_final + 255) & ~size_t(255)));
+        const hipError_t e =
+            hs > 1 ? sgmv_shrink_split(L.X, sl.A_pool, sl.rank, sl.scale, L.token_order, L.work, L.n_items, hs, hkc,
+                                       part, ext ? nullptr : hbuf, ext, K, L.r_max, st, tm)
+                   : sgmv_shrink(1, L.X, sl.A_pool, sl.rank, L.token_order, L.work, L.n_items, ext ? nullptr : hbuf,
+                                 K, L.r_max, st, tm, sl.scale, ext);
         if (e != hipSuccess) return e;
     }
-    if (g.bm == 256) {
-        const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
-        const bool epi = L.adapters && !f.ext, ktail = K % 32 != 0;
-        auto ker = epi ? (ktail ? gemm_dma_kernel<true, true> : gemm_dma_kernel<true, false>)
-                       : (ktail ? gemm_dma_kernel<false, true> : gemm_dma_kernel<false, false>);
-        return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(512), st, L.X, sl.W, sl.Y, M, N, K,
-                      tiles_m, tiles_n, f);
-    }
-    if (g.bm == 128) return launch_tiled<128, 128>(L.X, sl.W, sl.Y, M, N, K, f, st, tm);
-    return launch_tiled<64, 128>(L.X, sl.W, sl.Y, M, N, K, f, st, tm);
+    const bool epi = L.adapters && !f.ext;
+    if (g.bm == 256 && g.bn == 256) return launch_dma<256, 256, 2, 4, 64, 2>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256) return launch_dma<256, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 128) return launch_dma<128, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    return launch_dma<64, 128, 2, 2, 64, 4>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
 }
 
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {

@@ -83,6 +83,13 @@ hipError_t gemm_f32(const float* X, const float* W, float* Y, int M, int N, int 
 hipError_t sgmv_shrink(int dtype, const void* X, const void* A_pool, const int32_t* rank,
                        const int32_t* token_order, const int32_t* work, int n_items, float* h, int K, int r_max,
                        hipStream_t st, StageTimer* tm, const float* scale = nullptr, uint16_t* ext = nullptr);
+// The same over hs K ranges of hkc k each (few items, long K): fp32 planes in
+// part ([n_items * hs][16][r_max]), then h or ext as above.
+constexpr int kShrinkSplitMaxBlocks = 256;
+hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const float* scale,
+                             const int32_t* token_order, const int32_t* work, int n_items, int hs, int hkc,
+                             float* part, float* h, uint16_t* ext, int K, int r_max, hipStream_t st,
+                             StageTimer* tm);
 hipError_t sgmv_expand_f32(const float* h, const float* B_pool, const int32_t* rank, const float* scale,
                            const int32_t* token_order, const int32_t* work, int n_items, float* Y, int N, int r_max,
                            hipStream_t st, StageTimer* tm);

@@ -39,6 +39,59 @@ __global__ __launch_bounds__(WAVES * 64) void shrink_bf16_kernel(const uint16_t*
     shrink_item<WAVES>(X, A_pool, r, token_order, it, out, K, 0, K, r_max, red);
 }
 
+// Few items: grid n_items * hs, block b = kz * n_items + item computes its
+// item over K range kz (hkc k, 4 waves) into its own 16-row plane of part
+// ([n_items * hs][16][r_max] fp32); shrink_finish_kernel adds the planes in
+// kz order.
+__global__ __launch_bounds__(256) void shrink_split_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ A_pool,
+                                                           const int32_t* __restrict__ rank,
+                                                           const int32_t* __restrict__ token_order,
+                                                           const Item* __restrict__ work, float* __restrict__ part,
+                                                           int n_items, int hkc, int K, int r_max) {
+    __shared__ f32x4 red[4 * 4 * 64];
+    const int item = blockIdx.x % n_items, kz = blockIdx.x / n_items;
+    const Item it = work[item];
+    const int r = rank[it.slot];
+    if (r == 0) return;
+    ShrinkOut out{part + (int64_t)blockIdx.x * 16 * r_max, nullptr, 0, 0.f};
+    out.row0 = it.begin;
+    const int kbeg = kz * hkc, kend = min(K, kbeg + hkc);
+    shrink_item<4>(X, A_pool, r, token_order, it, out, K, kbeg, kend, r_max, red);
+}
+
+// h (fp32, or with ext the scaled bf16 hi / lo operand) of an item's rows:
+// its hs planes added in kz order; ranks past the slot's are zero.
+__global__ __launch_bounds__(256) void shrink_finish_kernel(const float* __restrict__ part,
+                                                            const int32_t* __restrict__ rank,
+                                                            const float* __restrict__ scale,
+                                                            const Item* __restrict__ work, float* __restrict__ h,
+                                                            uint16_t* __restrict__ ext, int n_items, int hs,
+                                                            int r_max) {
+    const Item it = work[blockIdx.x];
+    const int r = rank[it.slot];
+    if (r == 0) return;
+    const int rp = (r_max + 7) & ~7;
+    const int width = ext ? rp : r_max;
+    const float sc = ext ? scale[it.slot] : 0.f;
+    for (int i = threadIdx.x; i < 16 * width; i += blockDim.x) {
+        const int m = i / width, q = i - m * width;
+        if (m >= it.count) continue;
+        float v = 0.f;
+        if (q < r)
+            for (int kz = 0; kz < hs; ++kz) v += part[((int64_t)(kz * n_items + blockIdx.x) * 16 + m) * r_max + q];
+        const int64_t p = it.begin + m;
+        if (ext) {
+            v *= sc;
+            const uint16_t hi = f32_to_bf16(v);
+            ext[(p * 2) * rp + q] = hi;
+            ext[(p * 2 + 1) * rp + q] = f32_to_bf16(v - bf16_to_f32(hi));
+        } else {
+            h[p * r_max + q] = v;
+        }
+    }
+}
+
 // fp32 pools: one thread per (row, rank), plain fp32 FMA over K.
 __global__ __launch_bounds__(256) void shrink_f32_kernel(const float* __restrict__ X, const float* __restrict__ A_pool,
                                                          const int32_t* __restrict__ rank,
@@ -117,6 +170,18 @@ hipError_t sgmv_shrink(int dtype, const void* X, const void* A_pool, const int32
     }
     return launch(tm, "sgmv_shrink", shrink_f32_kernel, dim3(n_items), dim3(256), st, (const float*)X,
                   (const float*)A_pool, rank, token_order, (const Item*)work, h, K, r_max);
+}
+
+hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const float* scale,
+                             const int32_t* token_order, const int32_t* work, int n_items, int hs, int hkc,
+                             float* part, float* h, uint16_t* ext, int K, int r_max, hipStream_t st,
+                             StageTimer* tm) {
+    if (n_items == 0) return hipSuccess;
+    hipError_t e = launch(tm, "sgmv_shrink", shrink_split_kernel, dim3(n_items * hs), dim3(256), st, X, A_pool,
+                          rank, token_order, (const Item*)work, part, n_items, hkc, K, r_max);
+    if (e != hipSuccess) return e;
+    return launch(tm, "sgmv_shrink_finish", shrink_finish_kernel, dim3(n_items), dim3(256), st, (const float*)part,
+                  rank, scale, (const Item*)work, h, ext, n_items, hs, r_max);
 }
 
 hipError_t sgmv_expand_f32(const float* h, const float* B_pool, const int32_t* rank, const float* scale,

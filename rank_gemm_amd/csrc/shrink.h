@@ -26,10 +26,11 @@ struct Item {
 // extra K steps: scale_s * h split into bf16 hi and lo halves,
 // ext[p][0][q] = hi, ext[p][1][q] = lo, rows of 2 * rp elements.
 struct ShrinkOut {
-    float* h;          // [T][r_max] fp32 (when ext is null)
+    float* h;          // [T][r_max] fp32 (when ext is null), row p - row0
     uint16_t* ext;     // [T][2][rp] bf16 bits
     int rp;            // r_max rounded up to 8
     float scale;       // scale_s of the item's slot (ext only)
+    int row0 = 0;      // sorted position of h's first row
 };
 
 // red: LDS scratch of WAVES * 4 * 64 f32x4. Must be called by every thread of
@@ -113,7 +114,7 @@ __device__ __forceinline__ void shrink_item(const uint16_t* __restrict__ X, cons
                         out.ext[(p * 2 + 1) * out.rp + q] = f32_to_bf16(v - bf16_to_f32(hi));
                     }
                 } else if (q < r_max) {
-                    out.h[p * r_max + q] = s[e];
+                    out.h[(p - out.row0) * r_max + q] = s[e];
                 }
             }
         }

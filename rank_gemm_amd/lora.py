@@ -55,7 +55,7 @@ class SliceDesc(ctypes.Structure):
 
 class KernelStat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("count", ctypes.c_int32), ("mean_ms", ctypes.c_double),
-                ("min_ms", ctypes.c_double), ("max_ms", ctypes.c_double)]
+                ("min_ms", ctypes.c_double), ("max_ms", ctypes.c_double), ("median_ms", ctypes.c_double)]
 
 
 _lib = None
@@ -349,10 +349,11 @@ def profile_begin(max_records: int = 100000):
 
 
 def profile_end() -> dict:
-    """lora_profile_end: {kernel name: {count, mean_ms, min_ms, max_ms}}."""
+    """lora_profile_end: {kernel name: {count, mean_ms, min_ms, max_ms, median_ms}}."""
     cap = 32
     out = (KernelStat * cap)()
     n = _I()
     _check(lib().lora_profile_end(out, cap, ctypes.byref(n)), "lora_profile_end")
     return {out[i].name.decode(): {"count": out[i].count, "mean_ms": out[i].mean_ms, "min_ms": out[i].min_ms,
-                                   "max_ms": out[i].max_ms} for i in range(min(n.value, cap))}
+                                   "max_ms": out[i].max_ms, "median_ms": out[i].median_ms}
+            for i in range(min(n.value, cap))}

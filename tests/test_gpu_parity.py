@@ -166,6 +166,13 @@ EDGE = [
     (3900, 264, 4200, 4, [0, 3, 5, 2], 5, "bf16"),          # 256 x 256 tiles, r_max % 8 != 0: epilogue expand
     (4100, 256, 4000, 5, [0, 7, 2, 0, 6], 7, "bf16"),       # 256 x 256 tiles, epilogue expand, K % 32 == 0
     (64, 40960, 256, 2, [0, 16], 16, "bf16"),               # split-K, 20 GEMM splits, one adapter
+    (2000, 520, 4000, 5, [0, 16, 8, 16, 4], 16, "bf16"),     # 256 x 128 tiles: ragged T, d_out; K % 64 != 0
+    (2000, 264, 4000, 4, [0, 3, 5, 2], 5, "bf16"),          # 256 x 128 tiles, epilogue expand
+    (1000, 200, 4000, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # 128 x 128 tiles, 3 extension steps per slot
+    (500, 4104, 4000, 4, [0, 16, 3, 8], 16, "bf16"),         # 64 x 128 tiles, long K with a tail
+    (500, 256, 4000, 4, [0, 3, 5, 2], 5, "bf16"),           # 64 x 128 tiles, epilogue expand
+    (400, 2056, 4000, 5, [0, 80, 17, 0, 64], 80, "bf16"),    # few items: K-split shrink, 2 rank groups
+    (400, 2048, 4000, 4, [0, 3, 5, 2], 5, "bf16"),          # few items: K-split shrink to fp32 h
 ]
 
 
