@@ -278,6 +278,28 @@ def main():
              "note": "one-element fill kernel, 32 per graph: launch-to-launch floor of a replayed step"}
     log(f"warm: {warm}; floor: {floor}")
 
+    # ---- the same step with the plan built on the device --------------------------
+    # plan_device + 32 lora_linear_device_plan in one graph: no host work per step
+    ids_dev = torch.from_numpy(ids.copy()).cuda()
+    dplan = lora.plan_device(ids_dev, S)
+
+    def dev_step():
+        lora.plan_device(ids_dev, S, out=dplan)
+        for l in range(L):
+            lora.linear(xs[l], Ws[l], pools[l], dplan, y=ys[l], workspace=ws)
+
+    dstep_us = graph_us(dev_step, 1, reps=args.steps)
+
+    def plans_only():
+        for _ in range(L):
+            lora.plan_device(ids_dev, S, out=dplan)
+
+    plan_us = graph_us(plans_only, L)
+    device_plan = {"ms_per_step": round(dstep_us * 1e-3, 4), "tokens_per_s": round(T * L / (dstep_us * 1e-6), 1),
+                   "plan_kernel_us": round(plan_us, 3),
+                   "note": "lora_plan_device + 32 lora_linear_device_plan captured in one graph"}
+    log(f"device plan: {device_plan}")
+
     # ---- q/k/v in one call against three calls ----------------------------------
     slices = None
     if not args.no_slices:
@@ -466,7 +488,8 @@ def main():
                    "T": T, "d_in": d_in, "d_out": d_out, "S": S, "rank": 16, "layers": L,
                    "mode": "eager" if graph is None else "hip graph replay"},
         "roofline": roof, "cpu_baseline": cpu,
-        "correction": corr, "kernels": kernels, "warm": warm, "launch_floor": floor, "prefill": prefill,
+        "correction": corr, "kernels": kernels, "warm": warm, "launch_floor": floor, "device_plan": device_plan,
+        "prefill": prefill,
         "slices": slices, "other_configs": others,
     }
     print(json.dumps(out), flush=True)

@@ -141,6 +141,30 @@ int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_order, int32
 /* Upper bound on the work list length of any plan over T tokens, S slots. */
 int lora_plan_max_items(int T, int S);
 
+/*
+ * The same plan built on the device, for steps captured in a HIP graph (no
+ * host work, no host-to-device copy, no allocation, one kernel). Launch
+ * overhead is what drives engines to fixed-size buffers and graph capture
+ * ("LoRA serving, embeddings, rerankers, pooling", mlinterviewnotes.com,
+ * worked example in section "LoRA and speculative decoding"); the plan's
+ * content is that of lora_plan ("mstar.engine.resources.lora.pool",
+ * LoraAddressing).
+ *   slot_ids  dev int32 [T]
+ *   plan      dev int32 [lora_plan_device_words(T, S)], caller-owned, laid out
+ *             [work 4 * W][token_order T][slot_indptr S + 1][info 8] with
+ *             W = max(lora_plan_max_items(T, S), 1); work, token_order and
+ *             slot_indptr are bit-identical to lora_plan's for the same ids,
+ *             the work list is padded to W with empty items {0, 0, 0, 0}, and
+ *             info holds {T, S, T_a, k, n_items, max_seg, status, 0}
+ * 1 <= S <= LORA_DEVICE_PLAN_MAX_SLOTS. An id outside [0, S) cannot be
+ * reported at call time: it is planned as slot 0 (base output) and the
+ * status word becomes LORA_ESLOT. Asynchronous on `stream`.
+ * Errors: LORA_EINVAL (sizes, null pointers), LORA_EHIP.
+ */
+#define LORA_DEVICE_PLAN_MAX_SLOTS 4096
+size_t lora_plan_device_words(int T, int S);
+int lora_plan_device(int S, const int32_t* slot_ids, int T, int32_t* plan, void* stream);
+
 /* Device workspace lora_linear and lora_shrink need for T tokens. */
 size_t lora_workspace_bytes(const lora_pool* pool, int T);
 
@@ -167,6 +191,17 @@ size_t lora_workspace_bytes(const lora_pool* pool, int T);
 int lora_linear(const lora_pool* pool, const void* x, const void* W, const int32_t* token_order,
                 const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info, void* y,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lora_linear over a device plan from lora_plan_device (T tokens, the pool's
+ * S): the same kernels, launched for the plan's capacity W, with empty items
+ * exiting at once, so the host needs nothing from the plan and a captured
+ * graph stays valid for any token-to-slot assignment of T tokens. Rows on
+ * slot 0 equal the base output bit for bit, as with lora_linear.
+ * Workspace and errors as lora_linear.
+ */
+int lora_linear_device_plan(const lora_pool* pool, const void* x, const void* W, const int32_t* plan, int T,
+                            void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Several adapted projections that read the same x (a merged q/k/v or

@@ -288,6 +288,31 @@ int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t*
     return LORA_OK;
 }
 
+size_t lora_plan_device_words(int T, int S) {
+    if (T < 0 || S < 1 || S > LORA_DEVICE_PLAN_MAX_SLOTS) return 0;
+    const int cap = std::max(lora_plan_max_items(T, S), 1);
+    return 4 * (size_t)cap + (size_t)T + (size_t)S + 1 + 8;
+}
+
+int lora_plan_device(int S, const int32_t* slot_ids, int T, int32_t* plan, void* stream) {
+    if (S < 1 || S > LORA_DEVICE_PLAN_MAX_SLOTS || T < 0 || !plan || (T > 0 && !slot_ids)) return LORA_EINVAL;
+    const int cap = std::max(lora_plan_max_items(T, S), 1);
+    return lora::plan_device(slot_ids, T, S, cap, plan, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+int lora_linear_device_plan(const lora_pool* p, const void* x, const void* W, const int32_t* plan, int T, void* y,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (!p || !plan || T < 0 || p->S > LORA_DEVICE_PLAN_MAX_SLOTS) return LORA_EINVAL;
+    const int cap = std::max(lora_plan_max_items(T, p->S), 1);
+    const int32_t* work = plan;
+    const int32_t* token_order = plan + 4 * (size_t)cap;
+    const int32_t* slot_indptr = token_order + T;
+    // the host knows only the shapes: every row may carry an adapter, and the
+    // work list is launched at its capacity (padding items are on slot 0)
+    lora_plan_info info{T, p->S, T, 0, lora_plan_max_items(T, p->S), 0};
+    return lora_linear(p, x, W, token_order, slot_indptr, work, &info, y, workspace, workspace_bytes, stream);
+}
+
 size_t lora_workspace_bytes_multi(const lora_slice* slices, int n, int T) {
     if (T < 0 || check_slices(slices, n, nullptr, false) != LORA_OK) return 0;
     return multi_bytes(slices, n, T);

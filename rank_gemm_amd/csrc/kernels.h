@@ -76,6 +76,12 @@ size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max);
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm);
 hipError_t gemm_f32(const float* X, const float* W, float* Y, int M, int N, int K, hipStream_t st, StageTimer* tm);
 
+// ---- device planner -----------------------------------------------------------
+// plan: [work 4 * cap][token_order T][slot_indptr S + 1][info 8], work padded
+// to cap with empty items on slot 0; one workgroup.
+constexpr int kDevPlanMaxSlots = 4096;
+hipError_t plan_device(const int32_t* ids, int T, int S, int cap, int32_t* plan, hipStream_t st);
+
 // ---- SGMV shrink and the fp32 expand -----------------------------------------
 // h: fp32 [T][r_max] indexed by sorted position (rows of adapter items only).
 // With ext (bf16 pools only), writes the expand operand of the tiled GEMM's

@@ -29,8 +29,9 @@ EXPORTS = (
     "lora_pool_create", "lora_pool_destroy", "lora_pool_install", "lora_pool_clear", "lora_pool_rank",
     "lora_plan", "lora_plan_max_items", "lora_workspace_bytes", "lora_linear", "lora_shrink",
     "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_workspace_bytes_multi",
-    "lora_linear_multi",
+    "lora_linear_multi", "lora_plan_device_words", "lora_plan_device", "lora_linear_device_plan",
 )
+LORA_DEVICE_PLAN_MAX_SLOTS = 4096
 LORA_MAX_SLICES = 4
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -86,6 +87,10 @@ def lib():
             L.lora_workspace_bytes_multi.restype = _SZ
             L.lora_linear_multi.argtypes = [ctypes.POINTER(SliceDesc), _I, _P, _P, _P, _P, ctypes.POINTER(PlanInfo),
                                             _P, _SZ, _P]
+            L.lora_plan_device_words.argtypes = [_I, _I]
+            L.lora_plan_device_words.restype = _SZ
+            L.lora_plan_device.argtypes = [_I, _P, _I, _P, _P]
+            L.lora_linear_device_plan.argtypes = [_P, _P, _P, _P, _I, _P, _P, _SZ, _P]
             L.lora_shrink.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
             L.lora_profile_begin.argtypes = [_I]
             L.lora_profile_end.argtypes = [ctypes.POINTER(KernelStat), _I, ctypes.POINTER(_I)]
@@ -268,19 +273,70 @@ def plan_into(p: Plan, slot_ids) -> Plan:
     return p
 
 
-def linear(x: torch.Tensor, W: torch.Tensor, pool: Pool, p: Plan, y: torch.Tensor | None = None,
+class DevicePlan:
+    """A plan built on the device by lora_plan_device: one int32 buffer
+    [work 4 W][token_order T][slot_indptr S + 1][info 8]."""
+
+    def __init__(self, S: int, T: int, buf: torch.Tensor):
+        self.S, self.T, self.buf = S, T, buf
+        self.cap = max(int(lib().lora_plan_max_items(T, S)), 1)
+
+    def read(self) -> dict:
+        """Copy the plan to the host (synchronises): work (live items only),
+        token_order, slot_indptr and the info words."""
+        h = self.buf.cpu().numpy()
+        o = 4 * self.cap
+        info = h[o + self.T + self.S + 1:]
+        keys = ("T", "S", "T_a", "k", "n_items", "max_seg", "status")
+        d = {k: int(v) for k, v in zip(keys, info)}
+        d["work"] = h[:4 * d["n_items"]].reshape(-1, 4)
+        d["pad"] = h[4 * d["n_items"]:o].reshape(-1, 4)
+        d["token_order"] = h[o:o + self.T]
+        d["slot_indptr"] = h[o + self.T:o + self.T + self.S + 1]
+        return d
+
+
+def plan_device(slot_ids: torch.Tensor, S: int, out: DevicePlan | None = None) -> DevicePlan:
+    """lora_plan_device: plan device-resident int32 slot ids on the current
+    stream (no host work; graph-capturable). ``out`` reuses a buffer of the
+    same T and S."""
+    _dev_tensor(slot_ids, torch.int32, "slot_ids")
+    if slot_ids.dim() != 1:
+        raise ValueError("slot_ids must be 1-D")
+    T = int(slot_ids.shape[0])
+    words = int(lib().lora_plan_device_words(T, int(S)))
+    if words == 0:
+        raise ValueError(f"no device plan for T={T}, S={S} (1 <= S <= {LORA_DEVICE_PLAN_MAX_SLOTS})")
+    if out is None:
+        out = DevicePlan(int(S), T, torch.empty(words, dtype=torch.int32, device=slot_ids.device))
+    elif out.T != T or out.S != S:
+        raise ValueError("plan buffer has another T or S")
+    _check(lib().lora_plan_device(int(S), slot_ids.data_ptr(), T, out.buf.data_ptr(), _stream(slot_ids.device)),
+           "lora_plan_device")
+    return out
+
+
+def linear(x: torch.Tensor, W: torch.Tensor, pool: Pool, p, y: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """lora_linear: y = x W^T + per-row adapter correction."""
+    """lora_linear (host plan) or lora_linear_device_plan (DevicePlan):
+    y = x W^T + per-row adapter correction."""
     tdt = _TORCH_DTYPE[pool.dtype]
     T = p.T
     _dev_tensor(x, tdt, "x", (T, pool.d_in))
     _dev_tensor(W, tdt, "W", (pool.d_out, pool.d_in))
-    if p.dev is None:
-        raise ValueError("plan was not uploaded")
     if y is None:
         y = torch.empty((T, pool.d_out), dtype=tdt, device=x.device)
     _dev_tensor(y, tdt, "y", (T, pool.d_out))
     ws = workspace if workspace is not None else pool.workspace(T)
+    if isinstance(p, DevicePlan):
+        if p.S != pool.S:
+            raise ValueError("plan and pool have different S")
+        _check(lib().lora_linear_device_plan(pool.handle, x.data_ptr(), W.data_ptr(), p.buf.data_ptr(), T,
+                                             y.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                             _stream(x.device)), "lora_linear_device_plan")
+        return y
+    if p.dev is None:
+        raise ValueError("plan was not uploaded")
     to, ip, wk = p.dev_ptrs()
     _check(lib().lora_linear(pool.handle, x.data_ptr(), W.data_ptr(), to, ip, wk, ctypes.byref(p.info), y.data_ptr(),
                              ws.data_ptr(), ws.numel() * ws.element_size(), _stream(x.device)), "lora_linear")

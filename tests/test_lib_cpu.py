@@ -159,3 +159,21 @@ def test_multi_host_argument_errors():
     assert L.lora_workspace_bytes_multi(arr, 2, 10) == 0
     with pytest.raises(ValueError):
         lora.linear_multi(None, [], [], None)
+
+
+def test_device_plan_sizes_and_argument_errors():
+    """Sizes of the device plan buffer, and the host-side refusals of the
+    device planner and of lora_linear_device_plan (no kernel launched)."""
+    L = lora.lib()
+    # T = 64, S = 9: capacity 64 / 16 + 8 = 12 items -> 4 * 12 + 64 + 10 + 8 words
+    assert L.lora_plan_device_words(64, 9) == 4 * 12 + 64 + 10 + 8
+    assert L.lora_plan_device_words(0, 5) == 4 * 1 + 0 + 6 + 8
+    assert L.lora_plan_device_words(10, 0) == 0
+    assert L.lora_plan_device_words(-1, 5) == 0
+    assert L.lora_plan_device_words(10, lora.LORA_DEVICE_PLAN_MAX_SLOTS + 1) == 0
+    assert L.lora_plan_device(0, 1, 10, 1, None) == lora.LORA_EINVAL
+    assert L.lora_plan_device(5, 1, 10, None, None) == lora.LORA_EINVAL
+    assert L.lora_plan_device(5, None, 10, 1, None) == lora.LORA_EINVAL
+    assert L.lora_plan_device(5, 1, -1, 1, None) == lora.LORA_EINVAL
+    assert L.lora_plan_device(lora.LORA_DEVICE_PLAN_MAX_SLOTS + 1, 1, 10, 1, None) == lora.LORA_EINVAL
+    assert L.lora_linear_device_plan(None, 1, 1, 1, 10, 1, 1, 1 << 20, None) == lora.LORA_EINVAL
