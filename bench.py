@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-slices", action="store_true")
     ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--crossover", action="store_true",
+                    help="also time the SGMV shrink against the BGMV shrink over ranks, adapters and tokens per adapter")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 256 MiB device copies (reference for the FETCH_SIZE/WRITE_SIZE counters)")
@@ -105,6 +107,64 @@ def filler(torch, ms_target=60.0):
     for _ in range(n):
         a = torch.matmul(a, a) * 1e-2
     return a
+
+
+def shrink_crossover(torch, np, lora, K=4096):
+    """SGMV (lora_shrink: 16-row items, plan given) against BGMV
+    (lora_shrink_bgmv: token by token, no plan), both graph-replayed, warm."""
+    rows = []
+    g = np.random.default_rng(0)
+    cases = [(r, na, tpa, "uniform") for r in (8, 16, 64) for na in (4, 16, 64) for tpa in (1, 2, 4, 8, 16, 64)
+             if na * tpa <= 4096]
+    cases += [(16, 32, T // 32, "zipf") for T in (64, 512, 4096)]
+    for r, na, tpa, kind in cases:
+        T, S = na * tpa, na + 1
+        if kind == "uniform":
+            ids = np.repeat(np.arange(1, S, dtype=np.int32), tpa)
+            g.shuffle(ids)
+        else:
+            p = np.arange(1, S, dtype=np.float64) ** -1.1
+            ids = (g.choice(S - 1, size=T, p=p / p.sum()) + 1).astype(np.int32)
+        pool = lora.Pool(S, r, K, 64, "bf16")
+        A = (torch.randn(r, K, device="cuda") * 0.01).to(torch.bfloat16)
+        B = torch.zeros(64, r, device="cuda").to(torch.bfloat16)
+        for s in range(1, S):
+            pool.install(s, A, B, 2.0 * r)
+        x = torch.randn(T, K, device="cuda").to(torch.bfloat16)
+        plan = lora.plan(ids, S)
+        ids_dev = torch.from_numpy(ids).cuda()
+        ws = pool.workspace(T)
+        h = torch.empty(T, r, device="cuda")
+
+        def timed(fn, reps=20, calls=8):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(calls):
+                    fn()
+            gr.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * calls)
+
+        sg = timed(lambda: lora.shrink(x, pool, plan, h=h))
+        bg = timed(lambda: lora.shrink_bgmv(x, pool, ids_dev, h=h, workspace=ws))
+        rows.append({"rank": r, "adapters": na, "tokens_per_adapter": tpa if kind == "uniform" else None,
+                     "T": T, "slots": kind, "items": plan.info.n_items, "sgmv_us": round(sg, 2),
+                     "bgmv_us": round(bg, 2), "faster": "sgmv" if sg < bg else "bgmv"})
+        log(f"crossover {rows[-1]}")
+        del pool, A, B, x, h, ws
+    return rows
 
 
 def main():
@@ -412,6 +472,8 @@ def main():
                    "kernels": {k: round(v["mean_ms"] * 1e3, 2) for k, v in s3.items()}}
         log(f"prefill: {prefill}")
 
+    crossover = shrink_crossover(torch, np, lora) if args.crossover else None
+
     # ---- other configs, single cold calls ------------------------------------------
     others = None
     if not args.no_configs:
@@ -490,7 +552,7 @@ def main():
         "roofline": roof, "cpu_baseline": cpu,
         "correction": corr, "kernels": kernels, "warm": warm, "launch_floor": floor, "device_plan": device_plan,
         "prefill": prefill,
-        "slices": slices, "other_configs": others,
+        "slices": slices, "other_configs": others, "shrink_crossover": crossover,
     }
     print(json.dumps(out), flush=True)
 

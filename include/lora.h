@@ -257,6 +257,23 @@ int lora_shrink(const lora_pool* pool, const void* x, const int32_t* token_order
                 size_t workspace_bytes, void* stream);
 
 /*
+ * The shrink in BGMV form, for the SGMV / BGMV comparison: the same h as
+ * lora_shrink (token order, fp32 [T][r_max], zeros past each row's rank and
+ * on slot 0 or rank-0 slots), computed one token at a time from the raw slot
+ * map with no grouping and no plan: the batched gather matrix-vector kernel
+ * that "LoRA serving, embeddings, rerankers, pooling" (mlinterviewnotes.com)
+ * sets against the segmented SGMV, section "SGLang: chunked SGMV, and a
+ * rank-aware kernel". Each token reads its slot's A_s; SGMV reads A_s once
+ * per item of up to 16 tokens.
+ *   slot_ids  dev int32 [T]; ids outside [1, S) give zero rows
+ *   workspace dev, at least lora_workspace_bytes(pool, T) bytes
+ * bf16 pools only. Errors: LORA_EINVAL (fp32 pool, null pointer), LORA_ESPACE,
+ * LORA_EHIP.
+ */
+int lora_shrink_bgmv(const lora_pool* pool, const void* x, const int32_t* slot_ids, int T, float* h,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Per-kernel timing, for diagnostics and the benchmark's roofline figures.
  * Between lora_profile_begin and lora_profile_end, lora_linear,
  * lora_linear_multi and lora_shrink record a HIP event pair around every

@@ -33,12 +33,31 @@ inline size_t es_of(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-// workspace: the bf16 path's partial products and h; the fp32 path's h
+// K splits of the stand-alone shrinks: SGMV over few items (at most
+// kShrinkSplitMaxBlocks workgroups) and BGMV (one workgroup per token and split)
+inline void sgmv_split(int n_items, int K, int* hs, int* hkc) {
+    *hs = 1;
+    *hkc = K;
+    if (n_items >= lora::kShrinkSplitMaxBlocks / 2) return;
+    const int h = std::min(8, lora::kShrinkSplitMaxBlocks / std::max(n_items, 1));
+    *hkc = std::max(256, ((K + h - 1) / h + 31) / 32 * 32);
+    *hs = (K + *hkc - 1) / *hkc;
+}
+inline void bgmv_split(int T, int K, int* hs, int* hkc) {
+    const int h = std::max(1, std::min(8, 2048 / std::max(T, 1)));
+    *hkc = std::max(256, ((K + h - 1) / h + 31) / 32 * 32);
+    *hs = (K + *hkc - 1) / *hkc;
+}
+
+// workspace: the bf16 path's partial products and h, and the stand-alone
+// shrinks' h plus split planes; the fp32 path's h
 inline size_t h_bytes(const lora_pool* p, int T) {
     const size_t h = align256((size_t)T * p->r_max * sizeof(float));
     if (p->dtype != LORA_BF16) return h;
     const size_t g = lora::gemm_bf16_workspace(T, &p->d_out, 1, p->d_in, p->r_max);
-    return g > h ? g : h;
+    const size_t rows = std::max<size_t>({(size_t)lora::kShrinkSplitMaxBlocks * 16, 2048, (size_t)T});
+    const size_t s = h + align256(rows * p->r_max * sizeof(float));
+    return std::max(g, s);
 }
 
 static_assert(LORA_MAX_SLICES == lora::kMaxSlices, "slice limit of the interface and the kernels");
@@ -376,15 +395,44 @@ int lora_shrink(const lora_pool* p, const void* x, const int32_t* token_order, c
     if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
     hipStream_t st = as_stream(stream);
     float* hs = static_cast<float*>(workspace);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)T * p->r_max * 4));
     std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
     if (profiler().on) lk.lock();
     lora::StageTimer* tm = timer_for(st);
-    if (info->n_items > 0 && lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, hs,
-                                               p->d_in, p->r_max, st, tm) != hipSuccess)
-        return LORA_EHIP;
+    int ks = 1, kc = p->d_in;
+    if (p->dtype == LORA_BF16) sgmv_split(info->n_items, p->d_in, &ks, &kc);
+    if (info->n_items > 0) {
+        const hipError_t e =
+            ks > 1 ? lora::sgmv_shrink_split((const uint16_t*)x, (const uint16_t*)p->A, p->rank_dev, p->scale_dev,
+                                             token_order, work, info->n_items, ks, kc, part, hs, nullptr, p->d_in,
+                                             p->r_max, st, tm)
+                   : lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, hs, p->d_in,
+                                       p->r_max, st, tm);
+        if (e != hipSuccess) return LORA_EHIP;
+    }
     if (lora::scatter_h(hs, p->rank_dev, token_order, slot_indptr, p->S, h, T, p->r_max, st, tm) != hipSuccess)
         return LORA_EHIP;
     return LORA_OK;
+}
+
+int lora_shrink_bgmv(const lora_pool* p, const void* x, const int32_t* slot_ids, int T, float* h, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (!p || T < 0) return LORA_EINVAL;
+    if (p->dtype != LORA_BF16) return LORA_EINVAL;
+    if (T == 0) return LORA_OK;
+    if (!x || !slot_ids || !h) return LORA_EINVAL;
+    if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
+    hipStream_t st = as_stream(stream);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)T * p->r_max * 4));
+    int ks = 1, kc = p->d_in;
+    bgmv_split(T, p->d_in, &ks, &kc);
+    std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
+    if (profiler().on) lk.lock();
+    lora::StageTimer* tm = timer_for(st);
+    return lora::bgmv_shrink((const uint16_t*)x, (const uint16_t*)p->A, p->rank_dev, slot_ids, p->S, T, ks, kc, part,
+                             h, p->d_in, p->r_max, st, tm) == hipSuccess
+               ? LORA_OK
+               : LORA_EHIP;
 }
 
 int lora_profile_begin(int max_records) {

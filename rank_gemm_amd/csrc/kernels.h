@@ -96,6 +96,11 @@ hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const in
                              const int32_t* token_order, const int32_t* work, int n_items, int hs, int hkc,
                              float* part, float* h, uint16_t* ext, int K, int r_max, hipStream_t st,
                              StageTimer* tm);
+// BGMV shrink (token by token, no plan): planes part [hs][T][r_max], then h
+// [T][r_max] in token order.
+hipError_t bgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* slot_ids,
+                       int S, int T, int hs, int hkc, float* part, float* h, int K, int r_max, hipStream_t st,
+                       StageTimer* tm);
 hipError_t sgmv_expand_f32(const float* h, const float* B_pool, const int32_t* rank, const float* scale,
                            const int32_t* token_order, const int32_t* work, int n_items, float* Y, int N, int r_max,
                            hipStream_t st, StageTimer* tm);

@@ -92,6 +92,61 @@ __global__ __launch_bounds__(256) void shrink_finish_kernel(const float* __restr
     }
 }
 
+// BGMV shrink: one token at a time, no grouping (the batched gather
+// matrix-vector form that "LoRA serving, embeddings, rerankers, pooling"
+// contrasts with the segmented SGMV). grid (T, hs): block (t, kz) computes
+// x[t] . A_s[q] over K range kz for every q < r_s, s = slot_ids[t]; thread
+// (qi = tid / 16, ki = tid % 16) takes rank q0 + qi and every 16th 8-wide k
+// chunk, then 16-lane sums. Planes part[kz][t][q] (q < r_s only).
+__global__ __launch_bounds__(256) void bgmv_shrink_kernel(const uint16_t* __restrict__ X,
+                                                          const uint16_t* __restrict__ A_pool,
+                                                          const int32_t* __restrict__ rank,
+                                                          const int32_t* __restrict__ slot_ids, int S,
+                                                          float* __restrict__ part, int T, int hkc, int K,
+                                                          int r_max) {
+    const int t = blockIdx.x, kz = blockIdx.y;
+    const int s = slot_ids[t];
+    const int r = (s <= 0 || s >= S) ? 0 : rank[s];
+    if (r == 0) return;
+    const int qi = threadIdx.x >> 4, ki = threadIdx.x & 15;
+    const int kbeg = kz * hkc, kend = min(K, kbeg + hkc);
+    const uint16_t* xp = X + (int64_t)t * K;
+    for (int q0 = 0; q0 < r; q0 += 16) {
+        const int q = q0 + qi;
+        const uint16_t* ap = A_pool + ((int64_t)s * r_max + min(q, r - 1)) * K;
+        float acc = 0.f;
+        for (int k = kbeg + ki * 8; k < kend; k += 128) {
+            const u32x4 xv = *as_global<u32x4>(xp + k);
+            const u32x4 av = *as_global<u32x4>(ap + k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc = __builtin_fmaf(__uint_as_float(xv[e] << 16), __uint_as_float(av[e] << 16), acc);
+                acc = __builtin_fmaf(__uint_as_float(xv[e] & 0xffff0000u), __uint_as_float(av[e] & 0xffff0000u), acc);
+            }
+        }
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+        if (ki == 0 && q < r) part[((int64_t)kz * T + t) * r_max + q] = acc;
+    }
+}
+
+// h[t][q] (token order) = the planes of bgmv_shrink_kernel added in kz order
+// for q < r_s; zero past the rank and on slot 0 or a rank-0 slot.
+__global__ __launch_bounds__(256) void bgmv_finish_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ rank,
+                                                          const int32_t* __restrict__ slot_ids, int S,
+                                                          float* __restrict__ h, int T, int hs, int r_max) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)T * r_max) return;
+    const int t = (int)(i / r_max), q = (int)(i - (int64_t)t * r_max);
+    const int s = slot_ids[t];
+    const int r = (s <= 0 || s >= S) ? 0 : rank[s];
+    float v = 0.f;
+    if (q < r)
+        for (int kz = 0; kz < hs; ++kz) v += part[((int64_t)kz * T + t) * r_max + q];
+    h[i] = v;
+}
+
 // fp32 pools: one thread per (row, rank), plain fp32 FMA over K.
 __global__ __launch_bounds__(256) void shrink_f32_kernel(const float* __restrict__ X, const float* __restrict__ A_pool,
                                                          const int32_t* __restrict__ rank,
@@ -182,6 +237,18 @@ hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const in
     if (e != hipSuccess) return e;
     return launch(tm, "sgmv_shrink_finish", shrink_finish_kernel, dim3(n_items), dim3(256), st, (const float*)part,
                   rank, scale, (const Item*)work, h, ext, n_items, hs, r_max);
+}
+
+hipError_t bgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* slot_ids,
+                       int S, int T, int hs, int hkc, float* part, float* h, int K, int r_max, hipStream_t st,
+                       StageTimer* tm) {
+    if (T == 0) return hipSuccess;
+    hipError_t e = launch(tm, "bgmv_shrink", bgmv_shrink_kernel, dim3(T, hs), dim3(256), st, X, A_pool, rank,
+                          slot_ids, S, part, T, hkc, K, r_max);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)T * r_max;
+    return launch(tm, "bgmv_finish", bgmv_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
+                  (const float*)part, rank, slot_ids, S, h, T, hs, r_max);
 }
 
 hipError_t sgmv_expand_f32(const float* h, const float* B_pool, const int32_t* rank, const float* scale,

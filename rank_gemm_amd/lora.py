@@ -30,6 +30,7 @@ EXPORTS = (
     "lora_plan", "lora_plan_max_items", "lora_workspace_bytes", "lora_linear", "lora_shrink",
     "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_workspace_bytes_multi",
     "lora_linear_multi", "lora_plan_device_words", "lora_plan_device", "lora_linear_device_plan",
+    "lora_shrink_bgmv",
 )
 LORA_DEVICE_PLAN_MAX_SLOTS = 4096
 LORA_MAX_SLICES = 4
@@ -91,6 +92,7 @@ def lib():
             L.lora_plan_device_words.restype = _SZ
             L.lora_plan_device.argtypes = [_I, _P, _I, _P, _P]
             L.lora_linear_device_plan.argtypes = [_P, _P, _P, _P, _I, _P, _P, _SZ, _P]
+            L.lora_shrink_bgmv.argtypes = [_P, _P, _P, _I, _P, _P, _SZ, _P]
             L.lora_shrink.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
             L.lora_profile_begin.argtypes = [_I]
             L.lora_profile_end.argtypes = [ctypes.POINTER(KernelStat), _I, ctypes.POINTER(_I)]
@@ -396,6 +398,22 @@ def shrink(x: torch.Tensor, pool: Pool, p: Plan, h: torch.Tensor | None = None) 
     to, ip, wk = p.dev_ptrs()
     _check(lib().lora_shrink(pool.handle, x.data_ptr(), to, ip, wk, ctypes.byref(p.info), h.data_ptr(), ws.data_ptr(),
                              ws.numel(), _stream(x.device)), "lora_shrink")
+    return h
+
+
+def shrink_bgmv(x: torch.Tensor, pool: Pool, slot_ids: torch.Tensor, h: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """lora_shrink_bgmv: h [T, r_max] fp32 in token order from device slot ids (no plan)."""
+    tdt = _TORCH_DTYPE[pool.dtype]
+    _dev_tensor(slot_ids, torch.int32, "slot_ids")
+    T = int(slot_ids.shape[0])
+    _dev_tensor(x, tdt, "x", (T, pool.d_in))
+    if h is None:
+        h = torch.empty((T, pool.r_max), dtype=torch.float32, device=x.device)
+    _dev_tensor(h, torch.float32, "h", (T, pool.r_max))
+    ws = workspace if workspace is not None else pool.workspace(T)
+    _check(lib().lora_shrink_bgmv(pool.handle, x.data_ptr(), slot_ids.data_ptr(), T, h.data_ptr(), ws.data_ptr(),
+                                  ws.numel() * ws.element_size(), _stream(x.device)), "lora_shrink_bgmv")
     return h
 
 

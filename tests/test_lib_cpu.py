@@ -177,3 +177,8 @@ def test_device_plan_sizes_and_argument_errors():
     assert L.lora_plan_device(5, 1, -1, 1, None) == lora.LORA_EINVAL
     assert L.lora_plan_device(lora.LORA_DEVICE_PLAN_MAX_SLOTS + 1, 1, 10, 1, None) == lora.LORA_EINVAL
     assert L.lora_linear_device_plan(None, 1, 1, 1, 10, 1, 1, 1 << 20, None) == lora.LORA_EINVAL
+
+
+def test_bgmv_shrink_argument_errors():
+    L = lora.lib()
+    assert L.lora_shrink_bgmv(None, 1, 1, 4, 1, 1, 1 << 20, None) == lora.LORA_EINVAL
