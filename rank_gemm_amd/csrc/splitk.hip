@@ -248,15 +248,25 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
             }
         }
         issue_fence();  // round 1 is in flight
-        if constexpr (!LANE_META) {  // large pools: metadata staged in LDS
-            for (int i = tid; i <= S; i += kThreads) {
-                meta.indptr[i] = f.slot_indptr[i];
-                if (i < S) {
-                    meta.rank[i] = f.rank[i];
-                    meta.scale[i] = f.scale[i];
+        // large pools: metadata staged in LDS, or read in place past kMetaSlots
+        const int* m_indptr = meta.indptr;
+        const int* m_rank = meta.rank;
+        const float* m_scale = meta.scale;
+        if constexpr (!LANE_META) {
+            if (S <= kMetaSlots) {  // uniform
+                for (int i = tid; i <= S; i += kThreads) {
+                    meta.indptr[i] = f.slot_indptr[i];
+                    if (i < S) {
+                        meta.rank[i] = f.rank[i];
+                        meta.scale[i] = f.scale[i];
+                    }
                 }
+                __syncthreads();
+            } else {
+                m_indptr = f.slot_indptr;
+                m_rank = f.rank;
+                m_scale = f.scale;
             }
-            __syncthreads();
         }
         // slots of this lane's rows
         int sl[4] = {0, 0, 0, 0};
@@ -278,9 +288,9 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int p = p0 + (lane >> 4) * 4 + e;
-                sl[e] = p < M ? slot_of(meta.indptr, S, p) : 0;
-                rr[e] = sl[e] == 0 ? 0 : meta.rank[sl[e]];
-                sc[e] = meta.scale[sl[e]];
+                sl[e] = p < M ? slot_of(m_indptr, S, p) : 0;
+                rr[e] = sl[e] == 0 ? 0 : m_rank[sl[e]];
+                sc[e] = m_scale[sl[e]];
             }
         }
         const uint16_t* bp[4];

@@ -195,6 +195,23 @@ def test_edge_shapes(case):
     check_close(to_f64(y), ref, dtype, f"edge {EDGE[case]}", base)
 
 
+@pytest.mark.parametrize("T,d_out", [(64, 320), (600, 4096)])
+def test_pool_beyond_lds_metadata(T, d_out):
+    """More slots than the kernels stage in LDS (1024): the split-K epilogue
+    and the tiled epilogue read the slot metadata in place."""
+    S = 1100
+    g = np.random.default_rng(T)
+    ranks = np.where(g.random(S) < 0.9, 8, 0)
+    ranks[0] = 0
+    ids = g.integers(0, S, size=T).astype(np.int32)
+    ids[: T // 4] = g.integers(1030, S, size=T // 4)  # slots past 1024 are used
+    w = make_custom(300 + T, T, 256, d_out, S, ranks, 2.0 * ranks, ids, r_max=8)
+    proj = w.projections[0]
+    y, _, _ = run_layer(w, proj)
+    ref, base = oracle_pair(w, proj)
+    check_close(to_f64(y), ref, "bf16", f"S={S} T={T}", base)
+
+
 def test_all_rows_one_adapter_and_empty_T():
     w = make_custom(7, 64, 256, 128, 3, [0, 8, 0], [0, 16, 0], np.ones(64, np.int32))
     proj = w.projections[0]
