@@ -173,6 +173,8 @@ EDGE = [
     (500, 256, 4000, 4, [0, 3, 5, 2], 5, "bf16"),           # 64 x 128 tiles, epilogue expand
     (400, 2056, 4000, 5, [0, 80, 17, 0, 64], 80, "bf16"),    # few items: K-split shrink, 2 rank groups
     (400, 2048, 4000, 4, [0, 3, 5, 2], 5, "bf16"),          # few items: K-split shrink to fp32 h
+    (50, 512, 300, 4, [0, 256, 130, 1], 256, "bf16"),        # split-K, ranks past 64 (several B rounds)
+    (700, 264, 4096, 4, [0, 256, 130, 17], 256, "bf16"),     # 64 x 128 tiles, 8 extension steps per slot
 ]
 
 
