@@ -239,6 +239,11 @@ typedef struct lora_slice {
  * .y are not read); 0 when the pools cannot share a call. */
 size_t lora_workspace_bytes_multi(const lora_slice* slices, int n, int T);
 
+/* lora_linear_multi over a device plan from lora_plan_device (T tokens, the
+ * pools' S), as lora_linear_device_plan is to lora_linear. */
+int lora_linear_multi_device_plan(const lora_slice* slices, int n, const void* x, const int32_t* plan, int T,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 int lora_linear_multi(const lora_slice* slices, int n, const void* x, const int32_t* token_order,
                       const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info,
                       void* workspace, size_t workspace_bytes, void* stream);

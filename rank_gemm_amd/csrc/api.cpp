@@ -332,6 +332,20 @@ int lora_linear_device_plan(const lora_pool* p, const void* x, const void* W, co
     return lora_linear(p, x, W, token_order, slot_indptr, work, &info, y, workspace, workspace_bytes, stream);
 }
 
+int lora_linear_multi_device_plan(const lora_slice* slices, int n, const void* x, const int32_t* plan, int T,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_slices(slices, n, x, true);
+    if (rc != LORA_OK) return rc;
+    const lora_pool* p0 = slices[0].pool;
+    if (!plan || T < 0 || p0->S > LORA_DEVICE_PLAN_MAX_SLOTS) return LORA_EINVAL;
+    const int cap = std::max(lora_plan_max_items(T, p0->S), 1);
+    const int32_t* work = plan;
+    const int32_t* token_order = plan + 4 * (size_t)cap;
+    const int32_t* slot_indptr = token_order + T;
+    lora_plan_info info{T, p0->S, T, 0, lora_plan_max_items(T, p0->S), 0};
+    return lora_linear_multi(slices, n, x, token_order, slot_indptr, work, &info, workspace, workspace_bytes, stream);
+}
+
 size_t lora_workspace_bytes_multi(const lora_slice* slices, int n, int T) {
     if (T < 0 || check_slices(slices, n, nullptr, false) != LORA_OK) return 0;
     return multi_bytes(slices, n, T);

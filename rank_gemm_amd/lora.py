@@ -30,7 +30,7 @@ EXPORTS = (
     "lora_plan", "lora_plan_max_items", "lora_workspace_bytes", "lora_linear", "lora_shrink",
     "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_workspace_bytes_multi",
     "lora_linear_multi", "lora_plan_device_words", "lora_plan_device", "lora_linear_device_plan",
-    "lora_shrink_bgmv",
+    "lora_shrink_bgmv", "lora_linear_multi_device_plan",
 )
 LORA_DEVICE_PLAN_MAX_SLOTS = 4096
 LORA_MAX_SLICES = 4
@@ -92,6 +92,7 @@ def lib():
             L.lora_plan_device_words.restype = _SZ
             L.lora_plan_device.argtypes = [_I, _P, _I, _P, _P]
             L.lora_linear_device_plan.argtypes = [_P, _P, _P, _P, _I, _P, _P, _SZ, _P]
+            L.lora_linear_multi_device_plan.argtypes = [ctypes.POINTER(SliceDesc), _I, _P, _P, _I, _P, _SZ, _P]
             L.lora_shrink_bgmv.argtypes = [_P, _P, _P, _I, _P, _P, _SZ, _P]
             L.lora_shrink.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
             L.lora_profile_begin.argtypes = [_I]
@@ -369,7 +370,7 @@ def linear_multi(x: torch.Tensor, Ws, pools, p: Plan, ys=None, workspace: torch.
     tdt = _TORCH_DTYPE[pools[0].dtype]
     T = p.T
     _dev_tensor(x, tdt, "x", (T, pools[0].d_in))
-    if p.dev is None:
+    if not isinstance(p, DevicePlan) and p.dev is None:
         raise ValueError("plan was not uploaded")
     if ys is None:
         ys = [torch.empty((T, pl.d_out), dtype=tdt, device=x.device) for pl in pools]
@@ -380,6 +381,13 @@ def linear_multi(x: torch.Tensor, Ws, pools, p: Plan, ys=None, workspace: torch.
     if workspace is None:
         need = int(lib().lora_workspace_bytes_multi(arr, n, T))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if isinstance(p, DevicePlan):
+        if p.S != pools[0].S:
+            raise ValueError("plan and pools have different S")
+        _check(lib().lora_linear_multi_device_plan(arr, n, x.data_ptr(), p.buf.data_ptr(), T, workspace.data_ptr(),
+                                                   workspace.numel() * workspace.element_size(), _stream(x.device)),
+               "lora_linear_multi_device_plan")
+        return ys
     to, ip, wk = p.dev_ptrs()
     _check(lib().lora_linear_multi(arr, n, x.data_ptr(), to, ip, wk, ctypes.byref(p.info), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(x.device)),

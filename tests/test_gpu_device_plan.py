@@ -159,3 +159,45 @@ def test_graph_with_device_plan_follows_new_assignments():
         torch.cuda.synchronize()
         for l in range(LAYERS):
             assert torch.equal(ys[l].view(torch.int16), want[l].view(torch.int16)), f"assignment {rep} layer {l}"
+
+
+def test_multi_slice_over_device_plan_in_a_graph():
+    """q/k/v in one lora_linear_multi_device_plan call, planner and call
+    captured once; replays after new assignments equal the host-plan call."""
+    from rank_gemm_amd.inputs import make_qkv_decode
+
+    w = make_qkv_decode()
+    T, S = w.T, w.S
+    pools = [build_pool(w, pr) for pr in w.projections]
+    x = lora.to_device(w.projections[0].x, "bf16")
+    Ws = [lora.to_device(pr.W, "bf16") for pr in w.projections]
+    ys = [torch.empty((T, pr.d_out), dtype=torch.bfloat16, device="cuda") for pr in w.projections]
+    ws = torch.empty(lora.workspace_bytes_multi(pools, T), dtype=torch.uint8, device="cuda")
+    ids_dev = torch.from_numpy(w.slot_ids.copy()).cuda()
+    dp = lora.plan_device(ids_dev, S)
+
+    def step():
+        lora.plan_device(ids_dev, S, out=dp)
+        lora.linear_multi(x, Ws, pools, dp, ys=ys, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    g = np.random.default_rng(3)
+    for rep, ids in enumerate([w.slot_ids, g.integers(0, S, size=T).astype(np.int32), np.zeros(T, np.int32)]):
+        want = lora.linear_multi(x, Ws, pools, lora.plan(ids, S))
+        torch.cuda.synchronize()
+        for y in ys:
+            y.fill_(float("nan"))
+        ids_dev.copy_(torch.from_numpy(ids))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(ys[i].view(torch.int16), want[i].view(torch.int16)), f"assignment {rep} slice {i}"
