@@ -14,7 +14,6 @@ namespace lora {
 
 static inline __host__ __device__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
 struct Fuse {
@@ -60,10 +59,6 @@ __device__ __forceinline__ MetaView stage_meta(const Fuse& f, SlotMeta* sm) {
     }
     return MetaView{sm->indptr, sm->rank, sm->scale};
 }
-
-// 16-byte LDS chunk of (row, logical chunk c in 0..7). The XOR spreads the
-// 16 rows one MFMA operand read touches over distinct banks.
-__device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
 
 // Last slot s with slot_indptr[s] <= p (the slot whose segment holds p).
 __device__ __forceinline__ int slot_of(const int* indptr, int S, int p) {
