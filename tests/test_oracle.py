@@ -224,3 +224,28 @@ def test_bad_slot_rejected():
     slot_ids[2] = -1
     with pytest.raises(ValueError):
         oracle.lora_grouped("f32", x, W, 2, ads, slot_ids)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_slot_is_two_textbook_gemms(dtype):
+    """Every row on one slot: the layer is x W^T plus (alpha / r) (x A^T) B^T,
+    written here as plain triple loops over Python floats (no numpy product),
+    for all three oracle forms."""
+    T, d_in, d_out, r, alpha = 5, 6, 4, 3, 1.5
+    g = np.random.default_rng(31)
+    x = enc(g.standard_normal((T, d_in)), dtype)
+    W = enc(g.standard_normal((d_out, d_in)), dtype)
+    A = enc(g.standard_normal((r, d_in)), dtype)
+    B = enc(g.standard_normal((d_out, r)), dtype)
+    dec = (lambda a: bf16_to_f32(a).astype(float)) if dtype == "bf16" else (lambda a: np.asarray(a, float))
+    xf, Wf, Af, Bf = (dec(a).tolist() for a in (x, W, A, B))
+    y = [[0.0] * d_out for _ in range(T)]
+    for i in range(T):
+        h = [sum(xf[i][k] * Af[q][k] for k in range(d_in)) for q in range(r)]
+        for j in range(d_out):
+            base = sum(xf[i][k] * Wf[j][k] for k in range(d_in))
+            y[i][j] = base + (alpha / r) * sum(h[q] * Bf[j][q] for q in range(r))
+    ads = {1: Adapter(r, alpha, A, B)}
+    for form in FORMS:
+        got = run_form(form, dtype, x, W, 2, ads, np.ones(T, np.int32))
+        np.testing.assert_allclose(got, np.array(y), rtol=1e-12, atol=1e-12, err_msg=form)
