@@ -43,16 +43,15 @@ __device__ __forceinline__ void issue_fence() {
 // bf16 bit pattern -> float (exact)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// float -> bf16 bit pattern, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return uint16_t(u >> 16);
-}
+// float -> bf16 bit pattern, round to nearest, ties to even; NaN stays a
+// (quiet) NaN. gfx950 converts in hardware (v_cvt_pk_bf16_f32, two values
+// per instruction).
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    const bf16x2_hw v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // 16x16x32 bf16 matrix-core product: lane l supplies row (l % 16) of the

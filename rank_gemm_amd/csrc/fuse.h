@@ -70,8 +70,10 @@ __device__ __forceinline__ int slot_of(const int* indptr, int S, int p) {
     return lo;
 }
 
-// acc[i][j] covers sorted rows p0 + 16 i + (4 (lane/16) + e) and columns
-// n0 + 16 j + lane % 16. Adds scale_s * h[p] . B_s[n] for every adapter row.
+// acc[i][j][e] is sorted row p0 + 16 i + lane % 16, column n0 + 16 j +
+// 4 (lane / 16) + e (the products are taken as (W x^T) blocks, so that a lane
+// holds 4 consecutive columns of one row). Adds scale_s * h[p] . B_s[n] for
+// every adapter row.
 template <int FM, int FN>
 __device__ __forceinline__ void fused_expand(f32x4 (&acc)[FM][FN], const Fuse& f, const MetaView& mv, int p0,
                                              int n0, int M, int N, int lane) {
@@ -126,32 +128,61 @@ __device__ __forceinline__ void fused_expand(f32x4 (&acc)[FM][FN], const Fuse& f
                 const u32x2 alo{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    acc[i][j] = mfma16x16x16(ahi, bfr[j], acc[i][j]);
-                    acc[i][j] = mfma16x16x16(alo, bfr[j], acc[i][j]);
+                    acc[i][j] = mfma16x16x16(bfr[j], ahi, acc[i][j]);
+                    acc[i][j] = mfma16x16x16(bfr[j], alo, acc[i][j]);
                 }
             }
         }
     }
 }
 
-// Round and store: y[token_order[p]][n] for the rows and columns of acc.
+// Round and store through LDS (acc laid out as for fused_expand). The wave's
+// block is written to its staging area `stg` as bf16 rows of FN * 32 bytes in
+// 8-byte units (unit index XOR an even function of the row, against bank
+// conflicts), then read back as 16-byte row pieces, so that each store
+// instruction writes whole row segments y[token_order[p]][n .. n + 8). The
+// staging area is private to the wave: no barrier between the two halves.
 template <int FM, int FN>
-__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], uint16_t* __restrict__ Y,
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], char* stg, uint16_t* __restrict__ Y,
                                            const int32_t* __restrict__ token_order, int p0, int n0, int M, int N,
                                            int lane) {
+    constexpr int RB = FN * 32, U = FN * 4;      // row bytes, 8-byte units per row
+    constexpr int LPR = FN * 2, RPI = 64 / LPR;  // lanes per row, rows per read
+    static_assert(64 % LPR == 0 && (FM * 16) % RPI == 0, "staging layout");
+    constexpr int NR = FM * 16 / RPI;  // rows (read instructions) per lane
+    auto swz = [](int r) { return (2 * (r >> 1)) & (U - 2); };
+    // the output rows' token indices are loaded first: fetched between the
+    // stores, each would wait behind the store traffic of every CU
+    int tok[NR];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int t = 0; t < NR; ++t) tok[t] = token_order[min(p0 + t * RPI + lane / LPR, M - 1)];
+    const int c = lane & 15, q = lane >> 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int p = p0 + i * 16 + (lane >> 4) * 4 + e;
-            if (p >= M) continue;
-            uint16_t* yr = Y + (int64_t)token_order[p] * N;
+    for (int i = 0; i < FM; ++i) {
+        const int r = 16 * i + c;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = n0 + j * 16 + (lane & 15);
-                if (n < N) yr[n] = f32_to_bf16(acc[i][j][e]);
+        for (int j = 0; j < FN; ++j) {
+            const u32x2 v{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+            *reinterpret_cast<u32x2*>(stg + r * RB + ((4 * j + q) ^ swz(r)) * 8) = v;
+        }
+    }
+    const bool vec = (N & 7) == 0;  // rows of y are 16-byte aligned
+    const int u2 = lane % LPR;
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+        const int r = t * RPI + lane / LPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * RB + ((2 * u2) ^ swz(r)) * 8);
+        const int p = p0 + r, n = n0 + u2 * 8;
+        if (p < M && n < N) {
+            uint16_t* yp = Y + (int64_t)tok[t] * N + n;
+            if (vec) {
+                *reinterpret_cast<u32x4*>(yp) = v;
+            } else {
+                const int ne = min(8, N - n);
+                for (int e = 0; e < ne; ++e) yp[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
             }
         }
+    }
 }
 
 // Map a linear block id to (tile_m, tile_n). Consecutive ids go round-robin

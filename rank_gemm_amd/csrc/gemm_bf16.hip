@@ -30,29 +30,32 @@ namespace lora {
 
 // --------------------------------------------- tiled, direct-to-LDS loads --
 // BM x BN macro tiles over WM x WN waves, wave tile (BM / WM) x (BN / WN) of
-// 16 x 16 MFMA tiles; K in stages of BK (32 or 64) through NS LDS buffers,
-// filled by direct-to-LDS loads (global_load_lds_dwordx4: 16 B per lane,
-// written at the wave's LDS base + 16 * lane). A row of a stage is CPR = BK / 8
-// chunks of 16 B; one load instruction covers 64 / CPR rows. Lane i fetches
-// row i / CPR, chunk (i % CPR) ^ swizzle(row): the bank swizzle is applied by
-// choosing the source, so the MFMA fragment reads (row l % 16, chunk l / 16 of
-// a 32-k half) are free of bank conflicts. With BK = 64 each row piece is a
-// whole 128-byte line, so a stage costs half as many memory requests per byte
-// as with BK = 32. Stage kt + NS - 1 is loaded once every wave is past stage
-// kt's barrier. The fragment reads are issued and waited on by hand: with LDS
-// loads in flight the compiler would wait for all of them at the first use.
-template <int CPR>
-__device__ __forceinline__ int row_swz(int r) {
-    if constexpr (CPR == 8) return r & 7;
-    else return ((r >> 1) ^ (r >> 2)) & 3;
-}
+// 16 x 16 MFMA tiles; K in stages of 64 through NS LDS buffers, filled by
+// direct-to-LDS loads (global_load_lds_dwordx4: 16 B per lane, written at the
+// instruction's LDS base + 16 * lane). A row of a stage is one 128-byte line
+// (8 chunks of 16 B). Rows go in groups of 64; load instruction q (0..7) of a
+// group fetches rows q, q + 8, ..., q + 56, lane l taking chunk l % 8 of row
+// q + 8 (l / 8): every 8 lanes read one whole line in order, which the memory
+// pipeline sends as one 128-byte request. The instruction's 1 KB lands at
+// q * 1040 bytes into the group, and that 16-byte pad per instruction puts
+// rows q = 0..7 on 8 different bank offsets, so the MFMA fragment reads (row
+// r0 + l % 16, chunk l / 16 of a 32-k half) are free of bank conflicts.
+// Stage kt + NS - 1 is loaded once every wave is past stage kt's barrier. The
+// fragment reads are issued and waited on by hand: with LDS loads in flight
+// the compiler would wait for all of them at the first use.
+constexpr int kInstrBytes = 1040;              // 1 KB of 8 rows + 16 B pad
+constexpr int kGroupBytes = 8 * kInstrBytes;   // 64 rows
 
-// fragment I.. of N, read from consecutive fragment slots (STRIDE bytes apart) at `base`
-template <int I, int N, int STRIDE>
+// byte offset of the 16-row block starting at row r0 (r0 % 16 == 0)
+__host__ __device__ constexpr int block_off(int r0) { return (r0 / 64) * kGroupBytes + (r0 % 64) / 8 * 128; }
+
+// fragments I.. of N, 16-row blocks following the one at `base` (whose row
+// is a multiple of 16 * N, or of 64)
+template <int I, int N>
 __device__ __forceinline__ void read_frags(u32x4 (&fr)[N], uint32_t base) {
     if constexpr (I < N) {
-        fr[I] = lds_read16<I * STRIDE>(base);
-        read_frags<I + 1, N, STRIDE>(fr, base);
+        fr[I] = lds_read16<block_off(16 * I)>(base);
+        read_frags<I + 1, N>(fr, base);
     }
 }
 template <int N, int I, int FJ>
@@ -63,14 +66,16 @@ __device__ __forceinline__ void tie_frags(u32x4 (&fr)[FJ]) {
     }
 }
 // MFMA rows I.. of the wave tile; row i waits for A fragment i only (the B
-// fragments and A fragment 0 were waited on before row 0)
+// fragments and A fragment 0 were waited on before row 0). W is the left
+// operand: acc[i][j] is a block of (W x^T), a lane's 4 values are 4
+// consecutive output columns of one row.
 template <int I, int FI, int FJ>
 __device__ __forceinline__ void mfma_rows(f32x4 (&acc)[FI][FJ], u32x4 (&af)[FI], const u32x4 (&bf)[FJ]) {
     if constexpr (I < FI) {
         if constexpr (I > 0) lds_landed<FI - 1 - I>(af[I]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) acc[I][j] = mfma16x16x32(af[I], bf[j], acc[I][j]);
+        for (int j = 0; j < FJ; ++j) acc[I][j] = mfma16x16x32(bf[j], af[I], acc[I][j]);
         __builtin_amdgcn_sched_barrier(0);
         mfma_rows<I + 1, FI, FJ>(acc, af, bf);
     }
@@ -93,13 +98,14 @@ template <int BM, int BN, int WM, int WN, int BK, int NS, bool EPI, bool KTAIL>
 __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4))) void gemm_dma_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, Fuse f) {
-    constexpr int NW = WM * WN, CPR = BK / 8, RPI = 64 / CPR;  // chunks per row, rows per load instruction
-    constexpr int FI = BM / WM / 16, FJ = BN / WN / 16;        // MFMA tiles of a wave
-    constexpr int DA = BM / RPI / NW, DB = BN / RPI / NW;      // load instructions of a wave per stage
-    constexpr int DPW = DA + DB, STAGE = (BM + BN) * CPR;      // stage size in 16-byte chunks
-    constexpr int FSTRIDE = 16 * CPR * 16;                     // bytes between 16-row fragments
-    static_assert(BK == 32 || BK == 64, "stage depth");
-    static_assert(DA * NW * RPI == BM && DB * NW * RPI == BN, "load instructions per wave");
+    constexpr int NW = WM * WN;
+    constexpr int FI = BM / WM / 16, FJ = BN / WN / 16;   // MFMA tiles of a wave
+    constexpr int DA = BM / 8 / NW, DB = BN / 8 / NW;     // load instructions of a wave per stage
+    constexpr int DPW = DA + DB;
+    constexpr int ABYTES = BM / 64 * kGroupBytes, STAGE = (BM + BN) / 64 * kGroupBytes / 16;  // 16-byte units
+    static_assert(BK == 64 && BM % 64 == 0 && BN % 64 == 0, "stage layout");
+    static_assert((FI & (FI - 1)) == 0 && (FJ & (FJ - 1)) == 0, "fragment blocks");
+    static_assert(DA * NW * 8 == BM && DB * NW * 8 == BN, "load instructions per wave");
     static_assert(FI <= 16 && NS >= 2 && (NS - 2) * DPW < 64, "wait counters");
     __shared__ u32x4 lds[NS * STAGE];
     __shared__ SlotMeta meta;
@@ -113,19 +119,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     const int nk = (K + BK - 1) / BK;
     // this lane's rows of the A and B pieces it loads (rows past M or N are
     // clamped: their products land in outputs that are not stored)
-    const int rl = lane / CPR;
-    const int cl = (lane % CPR) ^ row_swz<CPR>(rl);
+    const int rl = lane >> 3, cl = lane & 7;
     int prow[DA], ncol[DB];
     const uint16_t* ap[DA];
     const uint16_t* bp[DB];
 #pragma unroll
     for (int b = 0; b < DA; ++b) {
-        prow[b] = m0 + (wave * DA + b) * RPI + rl;
+        const int u = wave * DA + b;  // load instruction: group u / 8, rows u % 8 + 8 i
+        prow[b] = m0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
         ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + cl * 8;
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-        ncol[b] = n0 + (wave * DB + b) * RPI + rl;
+        const int u = wave * DB + b;
+        ncol[b] = n0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
         bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
     }
     __syncthreads();  // slot metadata staged
@@ -197,9 +204,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
                 bsrc[b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
         }
 #pragma unroll
-        for (int b = 0; b < DA; ++b) dma16(asrc[b], st + (wave * DA + b) * 64);
+        for (int b = 0; b < DA; ++b) {
+            const int u = wave * DA + b;
+            dma16(asrc[b], st + ((u >> 3) * kGroupBytes + (u & 7) * kInstrBytes) / 16);
+        }
 #pragma unroll
-        for (int b = 0; b < DB; ++b) dma16(bsrc[b], st + BM * CPR + (wave * DB + b) * 64);
+        for (int b = 0; b < DB; ++b) {
+            const int u = wave * DB + b;
+            dma16(bsrc[b], st + (ABYTES + (u >> 3) * kGroupBytes + (u & 7) * kInstrBytes) / 16);
+        }
     };
 
     f32x4 acc[FI][FJ];
@@ -208,12 +221,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int fr = lane & 15, fc = lane >> 4;
-    uint32_t abase[BK / 32], bbase[BK / 32];  // per 32-k half of a stage
+    uint32_t abase[2], bbase[2];  // per 32-k half of a stage
+    const uint32_t lane_off = lds_offset(lds) + (fr & 7) * kInstrBytes + (fr >> 3) * 128;
 #pragma unroll
-    for (int h = 0; h < BK / 32; ++h) {
-        const int foff = fr * CPR + ((h * 4 + fc) ^ row_swz<CPR>(fr));
-        abase[h] = lds_offset(lds + wm * FI * 16 * CPR + foff);
-        bbase[h] = lds_offset(lds + BM * CPR + wn * FJ * 16 * CPR + foff);
+    for (int h = 0; h < 2; ++h) {
+        abase[h] = lane_off + block_off(wm * FI * 16) + (h * 4 + fc) * 16;
+        bbase[h] = lane_off + ABYTES + block_off(wn * FJ * 16) + (h * 4 + fc) * 16;
     }
 
 #pragma unroll
@@ -228,8 +241,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int h = 0; h < BK / 32; ++h) {
             u32x4 bf[FJ], af[FI];
-            read_frags<0, FJ, FSTRIDE>(bf, bbase[h] + so);
-            read_frags<0, FI, FSTRIDE>(af, abase[h] + so);
+            read_frags<0, FJ>(bf, bbase[h] + so);
+            read_frags<0, FI>(af, abase[h] + so);
             tie_frags<FI - 1, 0, FJ>(bf);
             lds_landed<FI - 1>(af[0]);
             mfma_rows<0, FI, FJ>(acc, af, bf);
@@ -237,7 +250,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     }
     const int p0 = m0 + wm * FI * 16, nb = n0 + wn * FJ * 16;
     if constexpr (EPI) fused_expand<FI, FJ>(acc, f, mv, p0, nb, M, N, lane);
-    store_tile<FI, FJ>(acc, Y, f.token_order, p0, nb, M, N, lane);
+    // the stage buffers become the output staging area once every wave is past its last fragment read
+    static_assert(NW * FI * FJ * 16 * 16 * 2 <= NS * STAGE * 16, "output staging");
+    __syncthreads();
+    store_tile<FI, FJ>(acc, reinterpret_cast<char*>(lds) + wave * (FI * 16) * (FJ * 32), Y, f.token_order, p0, nb,
+                       M, N, lane);
 }
 
 // ------------------------------------------------------------------ plan --
