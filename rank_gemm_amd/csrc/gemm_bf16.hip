@@ -25,6 +25,7 @@
 #include "fuse.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace lora {
 
@@ -257,6 +258,226 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
                        M, N, lane);
 }
 
+// ------------------------------------------------ 256 x 256 on 4 waves --
+// One wave per SIMD, wave tile 128 x 128 (8 x 8 MFMA blocks, 256 fp32
+// accumulators), the same two-stage direct-to-LDS ring and row-group layout
+// as above. With the 128 x 128 wave tile a stage reads 2/3 of the LDS bytes
+// of the 8-wave 128 x 64 tiling, and the single wave on a SIMD keeps the
+// matrix core busy by interleaving everything else between its MFMAs:
+//   phase A of stage kt: 64 MFMAs on the first 32-k half (fragments F0),
+//     one fragment read of the second half (F1) every 4 MFMAs;
+//   the wave's loads of stage kt + 1 landed; barrier;
+//   phase B: 64 MFMAs on F1, one fragment read of stage kt + 1's first half
+//     and one 1 KB load of stage kt + 2 (into stage kt's buffer, which every
+//     wave has finished reading) every 4 MFMAs.
+// The accumulators are tied to AGPRs by issuing these MFMAs as inline asm
+// (left to itself the register allocator shuffles accumulators through
+// VGPRs at every loop back edge, ~400 copies per stage). The compiler then
+// cannot see that those MFMAs read their fragment registers after issue:
+// every phase ends by keeping its fragments alive through two s_nop 7, so no
+// later instruction writes them while an MFMA may still read them, and 96
+// wait states separate the last MFMA from the first read of the accumulators.
+__device__ __forceinline__ void mfma_agpr(f32x4& acc, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void frags_landed(u32x4 (&a)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                 "+v"(a[6]), "+v"(a[7]));
+}
+__device__ __forceinline__ void frags_retire(const u32x4 (&a)[8], const u32x4 (&b)[8]) {
+    asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+                 "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]));
+}
+template <int G>
+struct Idx {
+    static constexpr int v = G;
+};
+template <class F, int... Gs>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, Gs...>, F&& fn) {
+    (fn(Idx<Gs>{}), ...);
+}
+
+template <bool EPI, bool KTAIL>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
+    int tiles_m, int tiles_n, Fuse f) {
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int ABYTES = BM / 64 * kGroupBytes, STAGE = (BM + BN) / 64 * kGroupBytes / 16;  // 16-byte units
+    __shared__ u32x4 lds[2 * STAGE];
+    __shared__ SlotMeta meta;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const MetaView mv = stage_meta(f, &meta);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int mend = min(M, m0 + BM);
+    const int nk = (K + BK - 1) / BK;
+    // wave w loads row group w of A and of B: instruction b fetches rows
+    // b + 8 i (rows past M or N are clamped; their outputs are not stored)
+    const int rl = lane >> 3, cl = lane & 7;
+    int prow[8], ncol[8];
+    const uint16_t* ap[8];
+    const uint16_t* bp[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        prow[b] = m0 + wave * 64 + b + 8 * rl;
+        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + cl * 8;
+        ncol[b] = n0 + wave * 64 + b + 8 * rl;
+        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
+    }
+    __syncthreads();  // slot metadata staged
+    const int nt = __builtin_amdgcn_readfirstlane(
+        nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0));
+    const int ne = nt - nk;
+    // cursor over the extra steps, read from the LDS copy of the slot metadata
+    // (as in gemm_dma_kernel)
+    auto md_indptr = [&](int i) { return meta.indptr[i]; };
+    auto md_rank = [&](int i) { return meta.rank[i]; };
+    const int spk = (2 * f.rp + BK - 1) / BK;
+    int cs = f.S, csb = 0, cse = 0, cr = 0, ct = 0;
+    auto seek = [&](int s) {
+        for (; s < f.S; ++s) {
+            const int sb = md_indptr(s), se = md_indptr(s + 1);
+            if (sb >= mend) {
+                s = f.S;
+                break;
+            }
+            const int r = md_rank(s);
+            if (s != 0 && r != 0 && se > m0 && se > sb) {
+                csb = sb;
+                cse = se;
+                cr = r;
+                break;
+            }
+        }
+        cs = s;
+        ct = 0;
+    };
+    if (ne > 0) {
+        int lo = 0, hi = f.S - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (md_indptr(mid) <= m0) lo = mid;
+            else hi = mid - 1;
+        }
+        seek(lo);
+    }
+    // sources of step kt's 16 load instructions (A 0..7, B 0..7); called once
+    // per step, in step order (the cursor advances on extra steps)
+    gptr<u32x4> src[16];
+    auto sources_base = [&](int kt) {
+        const int k = (kt - ne) * BK;
+        const bool kin = !KTAIL || k + cl * 8 < K;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            src[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
+            src[8 + b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
+        }
+    };
+    auto sources_extra = [&](int) {
+        const ExtraStep x{cs, csb, cse, cr, ct};
+        if (++ct == spk) seek(cs + 1);
+        const int k = x.t * BK + cl * 8;
+        const int q = k < f.rp ? k : k - f.rp;
+        const bool qin = k < 2 * f.rp && q < x.r;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            src[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
+            src[8 + b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+        }
+    };
+    u32x4* const dst = lds + (wave * kGroupBytes) / 16;
+    auto load_piece = [&](int g, int buf) {
+        dma16(src[g], dst + buf * STAGE + ((g < 8 ? 0 : ABYTES) + (g & 7) * kInstrBytes) / 16);
+    };
+    const int fr = lane & 15, fc = lane >> 4;
+    const uint32_t lane_off = lds_offset(lds) + (fr & 7) * kInstrBytes + (fr >> 3) * 128;
+    uint32_t abase[2], bbase[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        abase[h] = lane_off + block_off(wm * 128) + (h * 4 + fc) * 16;
+        bbase[h] = lane_off + ABYTES + block_off(wn * 128) + (h * 4 + fc) * 16;
+    }
+    u32x4 A0[8], B0[8], A1[8], B1[8];
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // steps 0 and 1 in flight, step 0 landed, its first half read
+    if (ne > 0) sources_extra(0);
+    else sources_base(0);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) load_piece(g, 0);
+    if (ne > 1) sources_extra(1);
+    else sources_base(min(1, nt - 1));
+#pragma unroll
+    for (int g = 0; g < 16; ++g) load_piece(g, 1);
+    vm_landed<16>();
+    stage_barrier();
+    static_for(std::make_integer_sequence<int, 8>{}, [&](auto jc) {
+        constexpr int j = decltype(jc)::v;
+        B0[j] = lds_read16<block_off(16 * j)>(bbase[0]);
+        A0[j] = lds_read16<block_off(16 * j)>(abase[0]);
+    });
+    // one step; `next` sets the sources of step kt + 2
+    auto step = [&](int kt, auto&& next) {
+        const uint32_t so = (kt & 1) * STAGE * 16, sn = ((kt & 1) ^ 1) * STAGE * 16;
+        frags_landed(A0);
+        frags_landed(B0);
+        // phase A
+        static_for(std::make_integer_sequence<int, 16>{}, [&](auto gc) {
+            constexpr int g = decltype(gc)::v;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (g < 8) B1[g] = lds_read16<block_off(16 * g)>(bbase[1] + so);
+            else A1[g - 8] = lds_read16<block_off(16 * (g - 8))>(abase[1] + so);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                constexpr int t0 = 4 * g;
+                mfma_agpr(acc[(t0 + u) >> 3][(t0 + u) & 7], B0[(t0 + u) & 7], A0[(t0 + u) >> 3]);
+            }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        frags_retire(A0, B0);
+        frags_landed(A1);
+        frags_landed(B1);
+        vm_landed<0>();  // step kt + 1 landed (this wave's loads)
+        stage_barrier();
+        // phase B
+        next(kt + 2);
+        static_for(std::make_integer_sequence<int, 16>{}, [&](auto gc) {
+            constexpr int g = decltype(gc)::v;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (g < 8) B0[g] = lds_read16<block_off(16 * g)>(bbase[0] + sn);
+            else A0[g - 8] = lds_read16<block_off(16 * (g - 8))>(abase[0] + sn);
+            load_piece(g, kt & 1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                constexpr int t0 = 4 * g;
+                mfma_agpr(acc[(t0 + u) >> 3][(t0 + u) & 7], B1[(t0 + u) & 7], A1[(t0 + u) >> 3]);
+            }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        frags_retire(A1, B1);
+    };
+    // steps whose step kt + 2 is an extra step, then the rest (the last two
+    // steps reload the last step: the load count per step stays fixed)
+    int kt = 0;
+    for (; kt + 2 < ne; ++kt) step(kt, sources_extra);
+    for (; kt < nt; ++kt) step(kt, [&](int s) { sources_base(min(s, nt - 1)); });
+    frags_landed(A0);
+    frags_landed(B0);
+    vm_landed<0>();
+#pragma unroll
+    for (int i = 0; i < 12; ++i) asm volatile("s_nop 7");  // last MFMA results written
+    const int p0 = m0 + wm * 128, nb = n0 + wn * 128;
+    if constexpr (EPI) fused_expand<8, 8>(acc, f, mv, p0, nb, M, N, lane);
+    __syncthreads();
+    store_tile<8, 8>(acc, reinterpret_cast<char*>(lds) + wave * 32768, Y, f.token_order, p0, nb, M, N, lane);
+}
+
 // ------------------------------------------------------------------ plan --
 GemmPlan gemm_bf16_plan(int M, int N, int K) {
     GemmPlan g{};
@@ -382,7 +603,13 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
         if (e != hipSuccess) return e;
     }
     const bool epi = L.adapters && !f.ext;
-    if (g.bm == 256 && g.bn == 256) return launch_dma<256, 256, 2, 4, 64, 2>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256 && g.bn == 256) {
+        const bool ktail = K % 64 != 0;
+        auto ker = epi ? (ktail ? gemm_w4_kernel<true, true> : gemm_w4_kernel<true, false>)
+                       : (ktail ? gemm_w4_kernel<false, true> : gemm_w4_kernel<false, false>);
+        return launch(tm, "gemm_bf16", ker, dim3(cdiv(M, 256) * cdiv(N, 256)), dim3(256), st, L.X, sl.W, sl.Y, M, N,
+                      K, cdiv(M, 256), cdiv(N, 256), f);
+    }
     if (g.bm == 256) return launch_dma<256, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     if (g.bm == 128) return launch_dma<128, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     return launch_dma<64, 128, 2, 2, 64, 4>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
