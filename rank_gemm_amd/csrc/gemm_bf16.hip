@@ -280,13 +280,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
 __device__ __forceinline__ void mfma_agpr(f32x4& acc, const u32x4& a, const u32x4& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void frags_landed(u32x4 (&a)[8]) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
-                 "+v"(a[6]), "+v"(a[7]));
+template <int N>
+__device__ __forceinline__ void frags_landed(u32x4 (&a)[N]) {
+    static_assert(N == 4 || N == 8, "fragment count");
+    if constexpr (N == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                     "+v"(a[6]), "+v"(a[7]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
-__device__ __forceinline__ void frags_retire(const u32x4 (&a)[8], const u32x4 (&b)[8]) {
-    asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
-                 "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]));
+template <int NB>
+__device__ __forceinline__ void frags_retire(const u32x4 (&a)[8], const u32x4 (&b)[NB]) {
+    static_assert(NB == 4 || NB == 8, "fragment count");
+    if constexpr (NB == 8)
+        asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
+                     "v"(a[6]), "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]),
+                     "v"(b[7]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
+                     "v"(a[6]), "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
 }
 template <int G>
 struct Idx {
@@ -297,13 +309,24 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, Gs...>, F&
     (fn(Idx<Gs>{}), ...);
 }
 
-template <bool EPI, bool KTAIL>
+// Tiles of 256 x BN (BN = 256 with 2 stages, or 128 with 3 stages: 150 KB).
+// Step kt + 2 is loaded during step kt. With 3 stages its buffer was last
+// read in step kt - 1, so its 1 KB loads are spread over both phases of step
+// kt; with 2 stages it is step kt's own buffer, free only in phase B.
+template <int BN, int NS, bool EPI, bool KTAIL>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, Fuse f) {
-    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int BM = 256, BK = 64;
+    constexpr int FI = 8, FJ = BN / 32;                    // MFMA blocks of a wave (128 x BN / 2)
+    constexpr int DA = 8, DB = BN / 32, ND = DA + DB;      // load instructions of a wave per step
+    constexpr int NM = FI * FJ, NR = FI + FJ;              // MFMAs and fragment reads per half step
     constexpr int ABYTES = BM / 64 * kGroupBytes, STAGE = (BM + BN) / 64 * kGroupBytes / 16;  // 16-byte units
-    __shared__ u32x4 lds[2 * STAGE];
+    static_assert((BN == 256 && NS == 2) || (BN == 128 && NS == 3), "tile configurations");
+    constexpr int NDA = NS == 3 ? ND / 2 : 0;              // loads of step kt + 2 issued in phase A
+    constexpr int NDB = ND - NDA;                          // ... and in phase B
+    static_assert(NDA + NDB < 64 && NR <= 16, "wait counters");
+    __shared__ u32x4 lds[NS * STAGE];
     __shared__ SlotMeta meta;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -313,17 +336,22 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int m0 = tm * BM, n0 = tn * BN;
     const int mend = min(M, m0 + BM);
     const int nk = (K + BK - 1) / BK;
-    // wave w loads row group w of A and of B: instruction b fetches rows
-    // b + 8 i (rows past M or N are clamped; their outputs are not stored)
+    // load instruction u of the tile fetches rows (u / 8) * 64 + u % 8 + 8 i
+    // (rows past M or N are clamped; their outputs are not stored)
     const int rl = lane >> 3, cl = lane & 7;
-    int prow[8], ncol[8];
-    const uint16_t* ap[8];
-    const uint16_t* bp[8];
+    int prow[DA], ncol[DB];
+    const uint16_t* ap[DA];
+    const uint16_t* bp[DB];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        prow[b] = m0 + wave * 64 + b + 8 * rl;
+    for (int b = 0; b < DA; ++b) {
+        const int u = wave * DA + b;
+        prow[b] = m0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
         ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + cl * 8;
-        ncol[b] = n0 + wave * 64 + b + 8 * rl;
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+        const int u = wave * DB + b;
+        ncol[b] = n0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
         bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
     }
     __syncthreads();  // slot metadata staged
@@ -363,17 +391,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
         seek(lo);
     }
-    // sources of step kt's 16 load instructions (A 0..7, B 0..7); called once
+    // sources of step kt's load instructions (A 0..DA-1, then B); set once
     // per step, in step order (the cursor advances on extra steps)
-    gptr<u32x4> src[16];
+    gptr<u32x4> src[ND];
     auto sources_base = [&](int kt) {
         const int k = (kt - ne) * BK;
         const bool kin = !KTAIL || k + cl * 8 < K;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            src[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
-            src[8 + b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
-        }
+        for (int b = 0; b < DA; ++b) src[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) src[DA + b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
     };
     auto sources_extra = [&](int) {
         const ExtraStep x{cs, csb, cse, cr, ct};
@@ -382,85 +409,98 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int q = k < f.rp ? k : k - f.rp;
         const bool qin = k < 2 * f.rp && q < x.r;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < DA; ++b)
             src[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
-            src[8 + b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
-        }
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+            src[DA + b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
     };
-    u32x4* const dst = lds + (wave * kGroupBytes) / 16;
     auto load_piece = [&](int g, int buf) {
-        dma16(src[g], dst + buf * STAGE + ((g < 8 ? 0 : ABYTES) + (g & 7) * kInstrBytes) / 16);
+        const int u = g < DA ? wave * DA + g : wave * DB + (g - DA);
+        dma16(src[g], lds + buf * STAGE + ((g < DA ? 0 : ABYTES) + (u >> 3) * kGroupBytes + (u & 7) * kInstrBytes) / 16);
     };
     const int fr = lane & 15, fc = lane >> 4;
     const uint32_t lane_off = lds_offset(lds) + (fr & 7) * kInstrBytes + (fr >> 3) * 128;
     uint32_t abase[2], bbase[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        abase[h] = lane_off + block_off(wm * 128) + (h * 4 + fc) * 16;
-        bbase[h] = lane_off + ABYTES + block_off(wn * 128) + (h * 4 + fc) * 16;
+        abase[h] = lane_off + block_off(wm * FI * 16) + (h * 4 + fc) * 16;
+        bbase[h] = lane_off + ABYTES + block_off(wn * FJ * 16) + (h * 4 + fc) * 16;
     }
-    u32x4 A0[8], B0[8], A1[8], B1[8];
-    f32x4 acc[8][8];
+    u32x4 A0[FI], B0[FJ], A1[FI], B1[FJ];
+    f32x4 acc[FI][FJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // steps 0 and 1 in flight, step 0 landed, its first half read
-    if (ne > 0) sources_extra(0);
-    else sources_base(0);
 #pragma unroll
-    for (int g = 0; g < 16; ++g) load_piece(g, 0);
-    if (ne > 1) sources_extra(1);
-    else sources_base(min(1, nt - 1));
+    for (int s0 = 0; s0 < 2; ++s0) {
+        if (s0 < ne) sources_extra(s0);
+        else sources_base(min(s0, nt - 1));
 #pragma unroll
-    for (int g = 0; g < 16; ++g) load_piece(g, 1);
-    vm_landed<16>();
+        for (int g = 0; g < ND; ++g) load_piece(g, s0);
+    }
+    vm_landed<ND>();
     stage_barrier();
-    static_for(std::make_integer_sequence<int, 8>{}, [&](auto jc) {
-        constexpr int j = decltype(jc)::v;
-        B0[j] = lds_read16<block_off(16 * j)>(bbase[0]);
-        A0[j] = lds_read16<block_off(16 * j)>(abase[0]);
+    static_for(std::make_integer_sequence<int, FI>{}, [&](auto ic) {
+        constexpr int i = decltype(ic)::v;
+        if constexpr (i < FJ) B0[i] = lds_read16<block_off(16 * i)>(bbase[0]);
+        A0[i] = lds_read16<block_off(16 * i)>(abase[0]);
     });
-    // one step; `next` sets the sources of step kt + 2
+    // fragment read r of a half: B blocks first (the first MFMAs need all of them)
+    auto read_half = [&](auto rc, u32x4 (&A)[FI], u32x4 (&B)[FJ], uint32_t ab, uint32_t bb) {
+        constexpr int r = decltype(rc)::v;
+        if constexpr (r < FJ) B[r] = lds_read16<block_off(16 * r)>(bb);
+        else A[r - FJ] = lds_read16<block_off(16 * (r - FJ))>(ab);
+    };
+    // one step; `next` sets the sources of step kt + 2, loaded into buffer bn
+    // (step kt's own buffer with 2 stages: only after every wave has read it)
+    int bc = 0, bn = 2 % NS;  // buffers of step kt and of step kt + 2
     auto step = [&](int kt, auto&& next) {
-        const uint32_t so = (kt & 1) * STAGE * 16, sn = ((kt & 1) ^ 1) * STAGE * 16;
+        const uint32_t so = bc * STAGE * 16, sn = (bc + 1 == NS ? 0 : bc + 1) * STAGE * 16;
+        next(kt + 2);
         frags_landed(A0);
         frags_landed(B0);
-        // phase A
-        static_for(std::make_integer_sequence<int, 16>{}, [&](auto gc) {
+        // phase A: MFMAs of the first half, reads of the second half
+        static_for(std::make_integer_sequence<int, NR>{}, [&](auto gc) {
             constexpr int g = decltype(gc)::v;
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (g < 8) B1[g] = lds_read16<block_off(16 * g)>(bbase[1] + so);
-            else A1[g - 8] = lds_read16<block_off(16 * (g - 8))>(abase[1] + so);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                constexpr int t0 = 4 * g;
-                mfma_agpr(acc[(t0 + u) >> 3][(t0 + u) & 7], B0[(t0 + u) & 7], A0[(t0 + u) >> 3]);
-            }
+            read_half(gc, A1, B1, abase[1] + so, bbase[1] + so);
+            static_for(std::make_integer_sequence<int, ND>{}, [&](auto pc) {  // loads of this group
+                constexpr int pi = decltype(pc)::v;
+                if constexpr (pi < NDA && pi * NR / NDA == g) load_piece(pi, bn);
+            });
+            static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {  // MFMAs of this group
+                constexpr int t = decltype(tc)::v;
+                if constexpr (t * NR / NM == g) mfma_agpr(acc[t / FJ][t % FJ], B0[t % FJ], A0[t / FJ]);
+            });
         });
         __builtin_amdgcn_sched_barrier(0);
         frags_retire(A0, B0);
         frags_landed(A1);
         frags_landed(B1);
-        vm_landed<0>();  // step kt + 1 landed (this wave's loads)
+        vm_landed<NDA>();  // step kt + 1 landed (this wave's loads; those of step kt + 2 issued above may not)
         stage_barrier();
-        // phase B
-        next(kt + 2);
-        static_for(std::make_integer_sequence<int, 16>{}, [&](auto gc) {
+        // phase B: MFMAs of the second half, reads of step kt + 1's first half, the other loads
+        static_for(std::make_integer_sequence<int, NR>{}, [&](auto gc) {
             constexpr int g = decltype(gc)::v;
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (g < 8) B0[g] = lds_read16<block_off(16 * g)>(bbase[0] + sn);
-            else A0[g - 8] = lds_read16<block_off(16 * (g - 8))>(abase[0] + sn);
-            load_piece(g, kt & 1);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                constexpr int t0 = 4 * g;
-                mfma_agpr(acc[(t0 + u) >> 3][(t0 + u) & 7], B1[(t0 + u) & 7], A1[(t0 + u) >> 3]);
-            }
+            read_half(gc, A0, B0, abase[0] + sn, bbase[0] + sn);
+            static_for(std::make_integer_sequence<int, ND>{}, [&](auto pc) {
+                constexpr int pi = decltype(pc)::v;
+                if constexpr (pi >= NDA && (pi - NDA) * NR / NDB == g) load_piece(pi, bn);
+            });
+            static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {
+                constexpr int t = decltype(tc)::v;
+                if constexpr (t * NR / NM == g) mfma_agpr(acc[t / FJ][t % FJ], B1[t % FJ], A1[t / FJ]);
+            });
         });
         __builtin_amdgcn_sched_barrier(0);
         frags_retire(A1, B1);
+        bc = bc + 1 == NS ? 0 : bc + 1;
+        bn = bn + 1 == NS ? 0 : bn + 1;
     };
     // steps whose step kt + 2 is an extra step, then the rest (the last two
     // steps reload the last step: the load count per step stays fixed)
@@ -472,10 +512,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     vm_landed<0>();
 #pragma unroll
     for (int i = 0; i < 12; ++i) asm volatile("s_nop 7");  // last MFMA results written
-    const int p0 = m0 + wm * 128, nb = n0 + wn * 128;
-    if constexpr (EPI) fused_expand<8, 8>(acc, f, mv, p0, nb, M, N, lane);
+    const int p0 = m0 + wm * FI * 16, nb = n0 + wn * FJ * 16;
+    if constexpr (EPI) fused_expand<FI, FJ>(acc, f, mv, p0, nb, M, N, lane);
+    static_assert(4 * FI * FJ * 16 * 16 * 2 <= NS * STAGE * 16, "output staging");
     __syncthreads();
-    store_tile<8, 8>(acc, reinterpret_cast<char*>(lds) + wave * 32768, Y, f.token_order, p0, nb, M, N, lane);
+    store_tile<FI, FJ>(acc, reinterpret_cast<char*>(lds) + wave * (FI * 16) * (FJ * 32), Y, f.token_order, p0, nb, M,
+                       N, lane);
 }
 
 // ------------------------------------------------------------------ plan --
@@ -571,6 +613,16 @@ static hipError_t launch_dma(const uint16_t* X, const uint16_t* W, uint16_t* Y, 
                   tiles_n, f);
 }
 
+template <int BN, int NS>
+static hipError_t launch_w4(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
+                            bool epi, hipStream_t st, StageTimer* tm) {
+    const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, BN);
+    const bool ktail = K % 64 != 0;
+    auto ker = epi ? (ktail ? gemm_w4_kernel<BN, NS, true, true> : gemm_w4_kernel<BN, NS, true, false>)
+                   : (ktail ? gemm_w4_kernel<BN, NS, false, true> : gemm_w4_kernel<BN, NS, false, false>);
+    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(256), st, X, W, Y, M, N, K, tiles_m, tiles_n, f);
+}
+
 // One slice on the tiled path: the shrink to final h, then the tiled GEMM
 // with the expand fused (r_max % 8 == 0: as extra K steps from scaled h as
 // bf16 hi / lo; otherwise in the epilogue from fp32 h).
@@ -603,14 +655,8 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
         if (e != hipSuccess) return e;
     }
     const bool epi = L.adapters && !f.ext;
-    if (g.bm == 256 && g.bn == 256) {
-        const bool ktail = K % 64 != 0;
-        auto ker = epi ? (ktail ? gemm_w4_kernel<true, true> : gemm_w4_kernel<true, false>)
-                       : (ktail ? gemm_w4_kernel<false, true> : gemm_w4_kernel<false, false>);
-        return launch(tm, "gemm_bf16", ker, dim3(cdiv(M, 256) * cdiv(N, 256)), dim3(256), st, L.X, sl.W, sl.Y, M, N,
-                      K, cdiv(M, 256), cdiv(N, 256), f);
-    }
-    if (g.bm == 256) return launch_dma<256, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256 && g.bn == 256) return launch_w4<256, 2>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256) return launch_w4<128, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     if (g.bm == 128) return launch_dma<128, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     return launch_dma<64, 128, 2, 2, 64, 4>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
 }

@@ -175,6 +175,8 @@ EDGE = [
     (400, 2048, 4000, 4, [0, 3, 5, 2], 5, "bf16"),          # few items: K-split shrink to fp32 h
     (50, 512, 300, 4, [0, 256, 130, 1], 256, "bf16"),        # split-K, ranks past 64 (several B rounds)
     (700, 264, 4096, 4, [0, 256, 130, 17], 256, "bf16"),     # 64 x 128 tiles, 8 extension steps per slot
+    (4096, 64, 4096, 4, [0, 16, 8, 4], 16, "bf16"),          # 256 x 256 tiles, a single K step
+    (4096, 40, 4096, 5, [0, 16, 3, 8, 0], 16, "bf16"),       # 256 x 256 tiles, K shorter than one step
 ]
 
 
