@@ -524,13 +524,27 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 GemmPlan gemm_bf16_plan(int M, int N, int K) {
     GemmPlan g{};
     if (M <= 0 || N <= 0 || K <= 0) return g;  // nothing to launch
-    // the largest macro tile that still gives most of the 256 CUs a tile
+    // tiled path: the macro tile with the least (rounds of 256 tiles) x (time
+    // of one tile); the relative tile times are measured ones (K = 4096:
+    // 256 x 256 96.5 us, 256 x 128 60 us, 128 x 128 47 us, 64 x 128 38 us)
     auto n_tiles = [&](int bm, int bn) { return (int64_t)cdiv(M, bm) * cdiv(N, bn); };
-    constexpr int64_t kFill = 200;
-    if (n_tiles(256, 256) >= kFill) { g.bm = 256; g.bn = 256; return g; }
-    if (n_tiles(256, 128) >= kFill) { g.bm = 256; g.bn = 128; return g; }
-    if (n_tiles(128, 128) >= kFill) { g.bm = 128; g.bn = 128; return g; }
-    if (M > 256 && n_tiles(64, 128) >= 128) { g.bm = 64; g.bn = 128; return g; }
+    if (n_tiles(256, 256) >= 200 || (M > 256 && n_tiles(64, 128) >= 128)) {
+        struct Cand {
+            int bm, bn;
+            double t;
+        };
+        constexpr Cand cands[] = {{256, 256, 96.5}, {256, 128, 60.0}, {128, 128, 47.0}, {64, 128, 38.0}};
+        double best = 0.0;
+        for (const Cand& c : cands) {
+            const double cost = (double)((n_tiles(c.bm, c.bn) + 255) / 256) * c.t;
+            if (g.bm == 0 || cost < best) {
+                best = cost;
+                g.bm = c.bm;
+                g.bn = c.bn;
+            }
+        }
+        return g;
+    }
     // split-K: 64 x 64 tiles, enough K splits for ~256 workgroups
     g.bm = 64; g.bn = 64;
     g.n_mt = cdiv(M, 64);

@@ -162,9 +162,9 @@ EDGE = [
     (2048, 256, 2048, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # tiled path, expand as extra K steps, 2 rank chunks
     (2048, 256, 2048, 4, [0, 3, 5, 2], 5, "bf16"),          # tiled path, r_max % 8 != 0: epilogue expand
     (4096, 128, 4096, 5, [0, 16, 8, 16, 4], 16, "bf16"),    # 256 x 256 tiles, long segments
-    (4000, 136, 4100, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # 256 x 256 tiles: ragged T, d_out, d_in; 5 extension steps
-    (3900, 264, 4200, 4, [0, 3, 5, 2], 5, "bf16"),          # 256 x 256 tiles, r_max % 8 != 0: epilogue expand
-    (4100, 256, 4000, 5, [0, 7, 2, 0, 6], 7, "bf16"),       # 256 x 256 tiles, epilogue expand, K % 32 == 0
+    (4000, 136, 3900, 6, [0, 80, 17, 0, 64, 3], 80, "bf16"),  # 256 x 256 tiles: ragged T, d_out, d_in; 5 extension steps
+    (3900, 264, 3880, 4, [0, 3, 5, 2], 5, "bf16"),          # 256 x 256 tiles, r_max % 8 != 0: epilogue expand
+    (4090, 256, 4000, 5, [0, 7, 2, 0, 6], 7, "bf16"),       # 256 x 256 tiles, epilogue expand, K % 32 == 0
     (64, 40960, 256, 2, [0, 16], 16, "bf16"),               # split-K, 20 GEMM splits, one adapter
     (2000, 520, 4000, 5, [0, 16, 8, 16, 4], 16, "bf16"),     # 256 x 128 tiles: ragged T, d_out; K % 64 != 0
     (2000, 264, 4000, 4, [0, 3, 5, 2], 5, "bf16"),          # 256 x 128 tiles, epilogue expand
