@@ -276,4 +276,11 @@ __device__ __forceinline__ void stage_barrier() {
 // concatenated columns (its n_nt is recomputed per slice).
 hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, hipStream_t st, StageTimer* tm);
 
+// Kernel 2 of the split-K path for one slice whose fp32 partials (ks splits,
+// the 64 x 64 tile layout of kernel 1) were written by another kernel: adds
+// the splits, applies the expand from fp32 h (h_splits planes of [M][r_max],
+// unscaled) and stores y.
+hipError_t splitk_finish_bf16(const LinearArgs& L, const SliceArgs& s, const float* part, int ks, int n_mt,
+                              const float* h, int h_splits, hipStream_t st, StageTimer* tm);
+
 }  // namespace lora

@@ -309,14 +309,27 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, Gs...>, F&
     (fn(Idx<Gs>{}), ...);
 }
 
+// Split over K (mid-sized T): block b takes tile b % n_tiles over the k
+// range [kz kc, (kz + 1) kc), kz = b / n_tiles, and writes fp32 partials in
+// the layout of the split-K path ([split][64-row tile][64-column tile][16
+// blocks of 16 x 16][64 lanes] f32x4, lane l holding rows 4 (l / 16) + e of
+// column l % 16). Split 0 also runs the expand's extra K steps, so the
+// split-K path's kernel 2 only adds the partials and rounds.
+struct SplitOut {
+    float* part;     // null: no split
+    int kc;          // k per split, a multiple of 64
+    int n_mt, n_nt;  // 64 x 64 tile grid of the partials
+};
+
 // Tiles of 256 x BN (BN = 256 with 2 stages, or 128 with 3 stages: 150 KB).
 // Step kt + 2 is loaded during step kt. With 3 stages its buffer was last
 // read in step kt - 1, so its 1 KB loads are spread over both phases of step
 // kt; with 2 stages it is step kt's own buffer, free only in phase B.
-template <int BN, int NS, bool EPI, bool KTAIL>
+template <int BN, int NS, bool EPI, bool KTAIL, bool SPLIT>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
-    int tiles_m, int tiles_n, Fuse f) {
+    int tiles_m, int tiles_n, Fuse f, SplitOut so) {
+    static_assert(!(SPLIT && EPI), "a split runs no expand");
     constexpr int BM = 256, BK = 64;
     constexpr int FI = 8, FJ = BN / 32;                    // MFMA blocks of a wave (128 x BN / 2)
     constexpr int DA = 8, DB = BN / 32, ND = DA + DB;      // load instructions of a wave per step
@@ -331,11 +344,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const MetaView mv = stage_meta(f, &meta);
+    const int n_tiles = tiles_m * tiles_n;
+    const int kz = SPLIT ? (int)blockIdx.x / n_tiles : 0;
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_coords(SPLIT ? (int)blockIdx.x - kz * n_tiles : (int)blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int mend = min(M, m0 + BM);
-    const int nk = (K + BK - 1) / BK;
+    const int kb = SPLIT ? kz * so.kc : 0;             // this block's k range [kb, kb + Kr)
+    const int Kr = SPLIT ? min(K - kb, so.kc) : K;
+    const int nk = (Kr + BK - 1) / BK;
     // load instruction u of the tile fetches rows (u / 8) * 64 + u % 8 + 8 i
     // (rows past M or N are clamped; their outputs are not stored)
     const int rl = lane >> 3, cl = lane & 7;
@@ -346,18 +363,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int b = 0; b < DA; ++b) {
         const int u = wave * DA + b;
         prow[b] = m0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + cl * 8;
+        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + kb + cl * 8;
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
         const int u = wave * DB + b;
         ncol[b] = n0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
+        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + kb + cl * 8;
     }
     __syncthreads();  // slot metadata staged
-    const int nt = __builtin_amdgcn_readfirstlane(
-        nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0));
-    const int ne = nt - nk;
+    // the expand's extra steps; in a split, split kz takes extra steps kz,
+    // kz + ks, kz + 2 ks, ... of the tile (the partials carry the correction)
+    const int ks = SPLIT ? (int)gridDim.x / n_tiles : 1;
+    const int ne_all = (f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0;
+    const int ne = __builtin_amdgcn_readfirstlane(SPLIT ? (ne_all > kz ? (ne_all - kz + ks - 1) / ks : 0) : ne_all);
+    const int nt = nk + ne;
     // cursor over the extra steps, read from the LDS copy of the slot metadata
     // (as in gemm_dma_kernel)
     auto md_indptr = [&](int i) { return meta.indptr[i]; };
@@ -391,20 +411,33 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         }
         seek(lo);
     }
+    auto advance = [&]() {
+        if (++ct == spk) seek(cs + 1);
+    };
+    if constexpr (SPLIT)
+        for (int e = 0; e < kz && ne > 0; ++e) advance();  // to this split's first extra step
     // sources of step kt's load instructions (A 0..DA-1, then B); set once
     // per step, in step order (the cursor advances on extra steps)
     gptr<u32x4> src[ND];
     auto sources_base = [&](int kt) {
         const int k = (kt - ne) * BK;
-        const bool kin = !KTAIL || k + cl * 8 < K;
+        const bool kin = !KTAIL || k + cl * 8 < Kr;
 #pragma unroll
         for (int b = 0; b < DA; ++b) src[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
 #pragma unroll
         for (int b = 0; b < DB; ++b) src[DA + b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
     };
+    // W is the left operand (acc holds blocks of W x^T, a lane 4 consecutive
+    // columns of one row) except in a split, whose partials take the split-K
+    // path's orientation (a lane 4 consecutive rows of one column)
+    auto mfma = [&](f32x4& c, const u32x4& a, const u32x4& w) {
+        if constexpr (SPLIT) mfma_agpr(c, a, w);
+        else mfma_agpr(c, w, a);
+    };
     auto sources_extra = [&](int) {
         const ExtraStep x{cs, csb, cse, cr, ct};
-        if (++ct == spk) seek(cs + 1);
+#pragma unroll 1
+        for (int e = 0; e < ks; ++e) advance();  // past the other splits' steps
         const int k = x.t * BK + cl * 8;
         const int q = k < f.rp ? k : k - f.rp;
         const bool qin = k < 2 * f.rp && q < x.r;
@@ -474,7 +507,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             });
             static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {  // MFMAs of this group
                 constexpr int t = decltype(tc)::v;
-                if constexpr (t * NR / NM == g) mfma_agpr(acc[t / FJ][t % FJ], B0[t % FJ], A0[t / FJ]);
+                if constexpr (t * NR / NM == g) mfma(acc[t / FJ][t % FJ], A0[t / FJ], B0[t % FJ]);
             });
         });
         __builtin_amdgcn_sched_barrier(0);
@@ -494,7 +527,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             });
             static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {
                 constexpr int t = decltype(tc)::v;
-                if constexpr (t * NR / NM == g) mfma_agpr(acc[t / FJ][t % FJ], B1[t % FJ], A1[t / FJ]);
+                if constexpr (t * NR / NM == g) mfma(acc[t / FJ][t % FJ], A1[t / FJ], B1[t % FJ]);
             });
         });
         __builtin_amdgcn_sched_barrier(0);
@@ -513,6 +546,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int i = 0; i < 12; ++i) asm volatile("s_nop 7");  // last MFMA results written
     const int p0 = m0 + wm * FI * 16, nb = n0 + wn * FJ * 16;
+    if constexpr (SPLIT) {
+        f32x4* out = reinterpret_cast<f32x4*>(so.part) + (int64_t)kz * so.n_mt * so.n_nt * 1024;
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+            const int rb = p0 / 16 + i;  // 16-row block
+            if ((rb >> 2) >= so.n_mt) continue;
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const int cb = nb / 16 + j;
+                if ((cb >> 2) >= so.n_nt) continue;
+                out[((int64_t)(rb >> 2) * so.n_nt + (cb >> 2)) * 1024 + ((rb & 3) * 4 + (cb & 3)) * 64 + lane] = acc[i][j];
+            }
+        }
+        return;
+    }
     if constexpr (EPI) fused_expand<FI, FJ>(acc, f, mv, p0, nb, M, N, lane);
     static_assert(4 * FI * FJ * 16 * 16 * 2 <= NS * STAGE * 16, "output staging");
     __syncthreads();
@@ -542,6 +590,31 @@ GemmPlan gemm_bf16_plan(int M, int N, int K) {
                 g.bm = c.bm;
                 g.bn = c.bn;
             }
+        }
+        // or 256 x 128 tiles split over K (few tiles, long K): each split's
+        // tile time scales with its k range, plus its fp32 partial writes (at
+        // 5 TB/s) and ~7 us of fill and drain; then the reduction reads the
+        // partials and writes y (at 4.4 TB/s, + 1 us). Measured: T = 512,
+        // 4096 -> 4096 28.5 + 8.1 us (no gain over 38 us unsplit);
+        // 14336 -> 4096 78 + 8 us against 122 us.
+        const double plain = best * K / 4096.0;
+        double best_split = 0.9 * plain;  // taken only when clearly cheaper
+        for (int ks = 2; ks <= 8; ks *= 2) {
+            const int kc = cdiv(cdiv(K, ks), 64) * 64;
+            const int kse = cdiv(K, kc);
+            if (kc < 512 || kse < 2) break;
+            const double part_bytes = kse * (double)M * N * 4.0;
+            const double cost = (double)((n_tiles(256, 128) * kse + 255) / 256) * 60.0 * kc / 4096.0 +
+                                part_bytes / 5.0e6 + 7.0 + (part_bytes + (double)M * N * 2.0) / 4.4e6 + 1.0;
+            if (cost < best_split) {
+                best_split = cost;
+                g.tks = kse;
+                g.tkc = kc;
+            }
+        }
+        if (g.tks > 1) {
+            g.bm = 256;
+            g.bn = 128;
         }
         return g;
     }
@@ -594,6 +667,12 @@ static bool joint_split(int M, const int* N, int n_slices, int K, GemmPlan* out)
     return g.nsub != 0;
 }
 
+// tiled path split over K: the partials, then the tiled path's h area
+static size_t split_tiled_workspace(int M, int N, const GemmPlan& g, int r_max) {
+    const size_t py = ((size_t)g.tks * cdiv(M, 64) * cdiv(N, 64) * 16 * 64 * 16 + 255) & ~size_t(255);
+    return py + tiled_workspace(M, r_max);
+}
+
 size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max) {
     if (M <= 0 || K <= 0 || n_slices < 1) return 0;
     GemmPlan gj;
@@ -608,7 +687,9 @@ size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max) 
     for (int i = 0; i < n_slices; ++i) {
         if (N[i] <= 0) continue;
         const GemmPlan g = gemm_bf16_plan(M, N[i], K);
-        const size_t b = g.nsub == 0 ? tiled_workspace(M, r_max) : split_workspace(M, g.n_nt, g, 1, r_max);
+        const size_t b = g.nsub != 0 ? split_workspace(M, g.n_nt, g, 1, r_max)
+                         : g.tks > 1 ? split_tiled_workspace(M, N[i], g, r_max)
+                                     : tiled_workspace(M, r_max);
         need = b > need ? b : need;
     }
     return need;
@@ -629,12 +710,76 @@ static hipError_t launch_dma(const uint16_t* X, const uint16_t* W, uint16_t* Y, 
 
 template <int BN, int NS>
 static hipError_t launch_w4(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
-                            bool epi, hipStream_t st, StageTimer* tm) {
+                            bool epi, hipStream_t st, StageTimer* tm, const SplitOut& so = SplitOut{}, int ks = 1) {
     const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, BN);
     const bool ktail = K % 64 != 0;
-    auto ker = epi ? (ktail ? gemm_w4_kernel<BN, NS, true, true> : gemm_w4_kernel<BN, NS, true, false>)
-                   : (ktail ? gemm_w4_kernel<BN, NS, false, true> : gemm_w4_kernel<BN, NS, false, false>);
-    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(256), st, X, W, Y, M, N, K, tiles_m, tiles_n, f);
+    auto ker = so.part ? (ktail ? gemm_w4_kernel<BN, NS, false, true, true> : gemm_w4_kernel<BN, NS, false, false, true>)
+               : epi   ? (ktail ? gemm_w4_kernel<BN, NS, true, true, false> : gemm_w4_kernel<BN, NS, true, false, false>)
+                       : (ktail ? gemm_w4_kernel<BN, NS, false, true, false> : gemm_w4_kernel<BN, NS, false, false, false>);
+    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n * (so.part ? ks : 1)), dim3(256), st, X, W, Y, M, N, K,
+                  tiles_m, tiles_n, f, so);
+}
+
+// The shrink of the tiled path, into fp32 h [M][r_max] or, with ext, the
+// expand operand of the extra K steps; ws: h_final bytes for h or ext, then
+// the K-split shrink's planes.
+static hipError_t tiled_shrink(const LinearArgs& L, const SliceArgs& sl, char* ws, float* h, uint16_t* ext,
+                               hipStream_t st, StageTimer* tm) {
+    const int M = L.M, K = L.K;
+    // few items over a long K: split K over more workgroups, then add the splits
+    int hs = 1, hkc = K;
+    if (L.n_items < kShrinkSplitMaxBlocks / 2) {
+        hs = min(8, kShrinkSplitMaxBlocks / max(L.n_items, 1));
+        hkc = max(256, (cdiv(K, hs) + 31) / 32 * 32);
+        hs = cdiv(K, hkc);
+    }
+    const size_t h_final = (size_t)M * ((L.r_max + 7) & ~7) * sizeof(float);
+    float* part = reinterpret_cast<float*>(ws + ((h_final + 255) & ~size_t(255)));
+    return hs > 1 ? sgmv_shrink_split(L.X, sl.A_pool, sl.rank, sl.scale, L.token_order, L.work, L.n_items, hs, hkc,
+                                      part, h, ext, K, L.r_max, st, tm)
+                  : sgmv_shrink(1, L.X, sl.A_pool, sl.rank, L.token_order, L.work, L.n_items, h, K, L.r_max, st, tm,
+                                sl.scale, ext);
+}
+
+// One slice on the tiled path split over K: the shrink to the expand operand,
+// the 256 x 128 kernel writing partials (split 0 with the extra K steps), then
+// the split-K path's kernel 2 without adapters (adds the partials, rounds).
+// Without the extra-step form of the expand (r_max % 8 != 0, or pools of more
+// than kMetaSlots slots), or when the extra steps would add more than a fifth
+// to a split, the slice runs unsplit.
+static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
+                                StageTimer* tm);
+static hipError_t split_tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
+                                      StageTimer* tm) {
+    const bool ext_ok = L.r_max % 8 == 0 && L.S <= kMetaSlots;
+    // extra steps per 256-row tile, bounded by the work items (16 rows of one
+    // slot each) that fall in 256 rows; spread over the splits they should
+    // stay small next to a split's base steps
+    const int64_t items_per_tile = ((int64_t)L.n_items * 256 + L.M - 1) / L.M;
+    const int64_t est_extra = (items_per_tile < L.S ? items_per_tile : (int64_t)L.S) * cdiv(2 * ((L.r_max + 7) & ~7), 64);
+    if (L.adapters && (!ext_ok || est_extra * 5 > (int64_t)g.tks * (g.tkc / 64))) {
+        GemmPlan gu = g;
+        gu.tks = 0;
+        return tiled_forward(L, sl, gu, st, tm);
+    }
+    const int M = L.M, N = sl.N, K = L.K;
+    const int n_mt = cdiv(M, 64), n_nt = cdiv(N, 64);
+    char* ws = static_cast<char*>(L.workspace);
+    const size_t py = ((size_t)g.tks * n_mt * n_nt * 16 * 64 * 16 + 255) & ~size_t(255);
+    float* part = reinterpret_cast<float*>(ws);
+    uint16_t* ext = reinterpret_cast<uint16_t*>(ws + py);
+    if (L.adapters) {
+        const hipError_t e = tiled_shrink(L, sl, ws + py, nullptr, ext, st, tm);
+        if (e != hipSuccess) return e;
+    }
+    const Fuse f{L.token_order, L.slot_indptr, nullptr, sl.B_pool, sl.rank, sl.scale, L.S, L.r_max, 1, 0, L.adapters,
+                 ext, (L.r_max + 7) & ~7};
+    const hipError_t e =
+        launch_w4<128, 3>(L.X, sl.W, nullptr, M, N, K, f, false, st, tm, SplitOut{part, g.tkc, n_mt, n_nt}, g.tks);
+    if (e != hipSuccess) return e;
+    LinearArgs base = L;
+    base.adapters = 0;
+    return splitk_finish_bf16(base, sl, part, g.tks, n_mt, nullptr, 1, st, tm);
 }
 
 // One slice on the tiled path: the shrink to final h, then the tiled GEMM
@@ -642,6 +787,7 @@ static hipError_t launch_w4(const uint16_t* X, const uint16_t* W, uint16_t* Y, i
 // bf16 hi / lo; otherwise in the epilogue from fp32 h).
 static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
                                 StageTimer* tm) {
+    if (g.tks > 1) return split_tiled_forward(L, sl, g, st, tm);
     const int M = L.M, N = sl.N, K = L.K;
     Fuse f{L.token_order, L.slot_indptr, nullptr, sl.B_pool, sl.rank, sl.scale, L.S, L.r_max, 1, 0, L.adapters,
            nullptr, (L.r_max + 7) & ~7};
@@ -652,20 +798,7 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
     f.h = ext ? nullptr : hbuf;
     f.ext = ext;
     if (L.adapters) {
-        // few items over a long K: split K over more workgroups, then add the splits
-        int hs = 1, hkc = K;
-        if (L.n_items < kShrinkSplitMaxBlocks / 2) {
-            hs = min(8, kShrinkSplitMaxBlocks / max(L.n_items, 1));
-            hkc = max(256, (cdiv(K, hs) + 31) / 32 * 32);
-            hs = cdiv(K, hkc);
-        }
-        const size_t h_final = (size_t)M * ((L.r_max + 7) & ~7) * sizeof(float);
-        float* part = reinterpret_cast<float*>(ws + ((h_final + 255) & ~size_t(255)));
-        const hipError_t e =
-            hs > 1 ? sgmv_shrink_split(L.X, sl.A_pool, sl.rank, sl.scale, L.token_order, L.work, L.n_items, hs, hkc,
-                                       part, ext ? nullptr : hbuf, ext, K, L.r_max, st, tm)
-                   : sgmv_shrink(1, L.X, sl.A_pool, sl.rank, L.token_order, L.work, L.n_items, ext ? nullptr : hbuf,
-                                 K, L.r_max, st, tm, sl.scale, ext);
+        const hipError_t e = tiled_shrink(L, sl, ws, ext ? nullptr : hbuf, ext, st, tm);
         if (e != hipSuccess) return e;
     }
     const bool epi = L.adapters && !f.ext;

@@ -462,4 +462,25 @@ hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, hipStream
                       g.n_mt, nt, M, f, sl);
 }
 
+hipError_t splitk_finish_bf16(const LinearArgs& L, const SliceArgs& s, const float* part, int ks, int n_mt,
+                              const float* h, int h_splits, hipStream_t st, StageTimer* tm) {
+    SliceTable sl{};
+    sl.n = 1;
+    sl.N[0] = s.N;
+    sl.W[0] = s.W;
+    sl.A_pool[0] = s.A_pool;
+    sl.B_pool[0] = s.B_pool;
+    sl.rank[0] = s.rank;
+    sl.scale[0] = s.scale;
+    sl.Y[0] = s.Y;
+    const int nt = cdiv(s.N, 64);
+    for (int i = 1; i <= kMaxSlices; ++i) sl.nt0[i] = nt;
+    const Fuse f{L.token_order, L.slot_indptr, h, nullptr, nullptr, nullptr, L.S, L.r_max, h_splits,
+                 (int64_t)L.M * L.r_max, L.adapters, nullptr, (L.r_max + 7) & ~7};
+    const dim3 eg(nt, 4 * n_mt);
+    const uint32_t shm = L.adapters ? (uint32_t)((16 * L.r_max + 32) * sizeof(float)) : 0u;
+    return launch_shm(tm, "gemm_splitk_epilogue", epilogue_for<false>(L), eg, dim3(kThreads), shm, st, part, ks,
+                      n_mt, nt, L.M, f, sl);
+}
+
 }  // namespace lora

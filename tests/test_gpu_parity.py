@@ -199,6 +199,30 @@ def test_edge_shapes(case):
     check_close(to_f64(y), ref, dtype, f"edge {EDGE[case]}", base)
 
 
+@pytest.mark.parametrize("S,r_max,split", [(9, 16, True), (70, 8, False), (9, 5, False)])
+def test_tiled_split_over_k(S, r_max, split):
+    """Mid-sized T with a long K runs the 256 x 128 tiled kernel split over K
+    (fp32 partials, the expand's extra K steps dealt round the splits) and the
+    split-K path's kernel 2 as the reduction; ragged d_out. The call runs
+    unsplit when the expand needs its fp32 epilogue form (r_max % 8 != 0) or
+    when many short segments would make the extra steps a large share."""
+    T, d_in, d_out = 512, 8192, 2100
+    g = np.random.default_rng(S)
+    ranks = np.minimum(g.integers(0, r_max + 1, size=S), r_max)
+    ranks[0] = 0
+    ranks[1] = r_max
+    ids = g.integers(0, S, size=T).astype(np.int32)
+    w = make_custom(400 + S, T, d_in, d_out, S, ranks, 2.0 * ranks, ids, r_max=r_max)
+    proj = w.projections[0]
+    pool = build_pool(w, proj)
+    lora.profile_begin()
+    y, _, _ = run_layer(w, proj, pool=pool)
+    stats = lora.profile_end()
+    assert "gemm_bf16" in stats and ("gemm_splitk_epilogue" in stats) == split, stats.keys()
+    ref, base = oracle_pair(w, proj)
+    check_close(to_f64(y), ref, "bf16", f"split tiled S={S} r_max={r_max}", base)
+
+
 @pytest.mark.parametrize("T,d_out", [(64, 320), (600, 4096)])
 def test_pool_beyond_lds_metadata(T, d_out):
     """More slots than the kernels stage in LDS (1024): the split-K epilogue
