@@ -240,6 +240,11 @@ typedef __attribute__((address_space(3))) u32x4* lds_u32x4_ptr;
 __device__ __forceinline__ void dma16(gptr<u32x4> src, u32x4* lds_dst) {
     __builtin_amdgcn_global_load_lds((gptr<void>)src, (lds_void_ptr)lds_dst, 16, 0, 0);
 }
+// the same with the non-temporal hint (data read once: kept out of the way of
+// what the caches should hold)
+__device__ __forceinline__ void dma16_nt(gptr<u32x4> src, u32x4* lds_dst) {
+    __builtin_amdgcn_global_load_lds((gptr<void>)src, (lds_void_ptr)lds_dst, 16, 0, 2);
+}
 __device__ __forceinline__ uint32_t lds_offset(const u32x4* p) { return (uint32_t)(uintptr_t)(lds_u32x4_ptr)p; }
 
 template <int OFF>

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) dma16(or_zero(kc[j] + k < K, xs[j] + k), st + (2 * wave + j) * 64);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dma16(or_zero(kc[j] + k < K, ws[j] + k), st + 512 + (2 * wave + j) * 64);
+        for (int j = 0; j < 2; ++j) dma16_nt(or_zero(kc[j] + k < K, ws[j] + k), st + 512 + (2 * wave + j) * 64);
     };
     // fragment reads: row r = lane % 16 of a 16-row tile, chunk 4 u + lane / 16
     const int fr = lane & 15, fq = lane >> 4;
