@@ -289,16 +289,19 @@ __device__ __forceinline__ void frags_landed(u32x4 (&a)[N]) {
     else
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
-template <int NB>
-__device__ __forceinline__ void frags_retire(const u32x4 (&a)[8], const u32x4 (&b)[NB]) {
-    static_assert(NB == 4 || NB == 8, "fragment count");
-    if constexpr (NB == 8)
+template <int NA, int NB>
+__device__ __forceinline__ void frags_retire(const u32x4 (&a)[NA], const u32x4 (&b)[NB]) {
+    static_assert((NA == 4 || NA == 8) && (NB == 4 || NB == 8), "fragment count");
+    if constexpr (NA == 8 && NB == 8)
         asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
                      "v"(a[6]), "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]),
                      "v"(b[7]));
-    else
+    else if constexpr (NA == 8)
         asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
                      "v"(a[6]), "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]),
+                     "v"(b[2]), "v"(b[3]));
 }
 template <int G>
 struct Idx {
@@ -321,22 +324,25 @@ struct SplitOut {
     int n_mt, n_nt;  // 64 x 64 tile grid of the partials
 };
 
-// Tiles of 256 x BN (BN = 256 with 2 stages, or 128 with 3 stages: 150 KB).
-// Step kt + 2 is loaded during step kt. With 3 stages its buffer was last
-// read in step kt - 1, so its 1 KB loads are spread over both phases of step
-// kt; with 2 stages it is step kt's own buffer, free only in phase B.
-template <int BN, int NS, bool EPI, bool KTAIL, bool SPLIT>
+// Tiles of BM x BN: 256 x 256 with 2 stages, 256 x 128 with 3 (150 KB). (A
+// 128 x 128 version on 4 waves, 64 x 64 wave tiles, took 57.7 us against
+// 47.3 us for the 8-wave kernel at T = 1024, 4096 -> 4096: with so few MFMAs
+// per phase one wave per SIMD hides too little.) Step kt + 2 is loaded during
+// step kt. With 3 stages its buffer was last read in step kt - 1, so its 1 KB
+// loads are spread over both phases of step kt; with 2 stages it is step kt's
+// own buffer, free only in phase B.
+template <int BM, int BN, int NS, bool EPI, bool KTAIL, bool SPLIT>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, Fuse f, SplitOut so) {
     static_assert(!(SPLIT && EPI), "a split runs no expand");
-    constexpr int BM = 256, BK = 64;
-    constexpr int FI = 8, FJ = BN / 32;                    // MFMA blocks of a wave (128 x BN / 2)
-    constexpr int DA = 8, DB = BN / 32, ND = DA + DB;      // load instructions of a wave per step
+    constexpr int BK = 64;
+    constexpr int FI = BM / 32, FJ = BN / 32;              // MFMA blocks of a wave (BM / 2 x BN / 2)
+    constexpr int DA = BM / 32, DB = BN / 32, ND = DA + DB;  // load instructions of a wave per step
     constexpr int NM = FI * FJ, NR = FI + FJ;              // MFMAs and fragment reads per half step
     constexpr int ABYTES = BM / 64 * kGroupBytes, STAGE = (BM + BN) / 64 * kGroupBytes / 16;  // 16-byte units
-    static_assert((BN == 256 && NS == 2) || (BN == 128 && NS == 3), "tile configurations");
-    constexpr int NDA = NS == 3 ? ND / 2 : 0;              // loads of step kt + 2 issued in phase A
+    static_assert((BM == 256 && BN == 256 && NS == 2) || (BM == 256 && BN == 128 && NS == 3), "tile configurations");
+    constexpr int NDA = NS >= 3 ? ND / 2 : 0;              // loads of step kt + 2 issued in phase A
     constexpr int NDB = ND - NDA;                          // ... and in phase B
     static_assert(NDA + NDB < 64 && NR <= 16, "wait counters");
     __shared__ u32x4 lds[NS * STAGE];
@@ -477,10 +483,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     vm_landed<ND>();
     stage_barrier();
-    static_for(std::make_integer_sequence<int, FI>{}, [&](auto ic) {
+    static_for(std::make_integer_sequence<int, (FI > FJ ? FI : FJ)>{}, [&](auto ic) {
         constexpr int i = decltype(ic)::v;
         if constexpr (i < FJ) B0[i] = lds_read16<block_off(16 * i)>(bbase[0]);
-        A0[i] = lds_read16<block_off(16 * i)>(abase[0]);
+        if constexpr (i < FI) A0[i] = lds_read16<block_off(16 * i)>(abase[0]);
     });
     // fragment read r of a half: B blocks first (the first MFMAs need all of them)
     auto read_half = [&](auto rc, u32x4 (&A)[FI], u32x4 (&B)[FJ], uint32_t ab, uint32_t bb) {
@@ -708,16 +714,23 @@ static hipError_t launch_dma(const uint16_t* X, const uint16_t* W, uint16_t* Y, 
                   tiles_n, f);
 }
 
-template <int BN, int NS>
+template <int BM, int BN, int NS, bool SPLIT_OK>
 static hipError_t launch_w4(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
                             bool epi, hipStream_t st, StageTimer* tm, const SplitOut& so = SplitOut{}, int ks = 1) {
-    const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, BN);
+    const int tiles_m = cdiv(M, BM), tiles_n = cdiv(N, BN);
     const bool ktail = K % 64 != 0;
-    auto ker = so.part ? (ktail ? gemm_w4_kernel<BN, NS, false, true, true> : gemm_w4_kernel<BN, NS, false, false, true>)
-               : epi   ? (ktail ? gemm_w4_kernel<BN, NS, true, true, false> : gemm_w4_kernel<BN, NS, true, false, false>)
-                       : (ktail ? gemm_w4_kernel<BN, NS, false, true, false> : gemm_w4_kernel<BN, NS, false, false, false>);
-    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n * (so.part ? ks : 1)), dim3(256), st, X, W, Y, M, N, K,
-                  tiles_m, tiles_n, f, so);
+    decltype(&gemm_w4_kernel<BM, BN, NS, false, false, false>) ker;
+    if constexpr (SPLIT_OK) {
+        if (so.part) {
+            ker = ktail ? gemm_w4_kernel<BM, BN, NS, false, true, true> : gemm_w4_kernel<BM, BN, NS, false, false, true>;
+            return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n * ks), dim3(256), st, X, W, Y, M, N, K,
+                          tiles_m, tiles_n, f, so);
+        }
+    }
+    ker = epi ? (ktail ? gemm_w4_kernel<BM, BN, NS, true, true, false> : gemm_w4_kernel<BM, BN, NS, true, false, false>)
+              : (ktail ? gemm_w4_kernel<BM, BN, NS, false, true, false> : gemm_w4_kernel<BM, BN, NS, false, false, false>);
+    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(256), st, X, W, Y, M, N, K, tiles_m, tiles_n,
+                  f, SplitOut{});
 }
 
 // The shrink of the tiled path, into fp32 h [M][r_max] or, with ext, the
@@ -775,7 +788,8 @@ static hipError_t split_tiled_forward(const LinearArgs& L, const SliceArgs& sl, 
     const Fuse f{L.token_order, L.slot_indptr, nullptr, sl.B_pool, sl.rank, sl.scale, L.S, L.r_max, 1, 0, L.adapters,
                  ext, (L.r_max + 7) & ~7};
     const hipError_t e =
-        launch_w4<128, 3>(L.X, sl.W, nullptr, M, N, K, f, false, st, tm, SplitOut{part, g.tkc, n_mt, n_nt}, g.tks);
+        launch_w4<256, 128, 3, true>(L.X, sl.W, nullptr, M, N, K, f, false, st, tm, SplitOut{part, g.tkc, n_mt, n_nt},
+                                     g.tks);
     if (e != hipSuccess) return e;
     LinearArgs base = L;
     base.adapters = 0;
@@ -802,8 +816,8 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
         if (e != hipSuccess) return e;
     }
     const bool epi = L.adapters && !f.ext;
-    if (g.bm == 256 && g.bn == 256) return launch_w4<256, 2>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
-    if (g.bm == 256) return launch_w4<128, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256 && g.bn == 256) return launch_w4<256, 256, 2, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256) return launch_w4<256, 128, 3, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     if (g.bm == 128) return launch_dma<128, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     return launch_dma<64, 128, 2, 2, 64, 4>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
 }
