@@ -509,8 +509,11 @@ def main():
                     gbs = kb / (sc["gemm_splitk"]["median_ms"] * 1e-3) / 1e9
                     entry["kernel1_frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
                 else:
+                    # the tiled GEMM, and when it is split over K, the reduction of its partials
+                    gemm_ms = sc["gemm_bf16"]["median_ms"] + (sc["gemm_splitk_epilogue"]["median_ms"]
+                                                              if "gemm_splitk_epilogue" in sc else 0.0)
                     fl = acc.base_flops(wc.T, pr.d_in, pr.d_out)
-                    tf = fl / (sc["gemm_bf16"]["median_ms"] * 1e-3) / 1e12
+                    tf = fl / (gemm_ms * 1e-3) / 1e12
                     entry["gemm_frac_mfma"] = round(tf / BF16_PEAK_TFLOPS, 4)
                 others[f"config{cfg} {pr.name}"] = entry
                 del pool_c, xc, Wc, yc
