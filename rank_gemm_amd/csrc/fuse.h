@@ -175,8 +175,8 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[FM][FN], char* stg
         const int p = p0 + r, n = n0 + u2 * 8;
         if (p < M && n < N) {
             uint16_t* yp = Y + (int64_t)tok[t] * N + n;
-            if (vec) {
-                *reinterpret_cast<u32x4*>(yp) = v;
+            if (vec) {  // non-temporal: the output is written once and not read back here
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(yp));
             } else {
                 const int ne = min(8, N - n);
                 for (int e = 0; e < ne; ++e) yp[e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
