@@ -214,6 +214,53 @@ struct ExtraStep {
     int s, sb, se, r, t;
 };
 
+// Cursor over a tile's extra steps (slot, its segment, rank, step within the
+// slot), advanced once per extra step issued. The slot metadata is read from
+// its LDS copy (the host takes the extra-step form only for pools of at most
+// kMetaSlots slots): a flat or global load here would also wait for every
+// direct-to-LDS load in flight.
+typedef const __attribute__((address_space(3))) SlotMeta* lds_meta_ptr;
+struct ExtraCursor {
+    lds_meta_ptr meta;
+    int S, m0, mend, spk;  // slots, the tile's rows [m0, mend), extra steps per slot
+    int cs, csb, cse, cr, ct;
+    __device__ __forceinline__ ExtraCursor(lds_meta_ptr m, int S_, int m0_, int mend_, int spk_)
+        : meta(m), S(S_), m0(m0_), mend(mend_), spk(spk_), cs(S_), csb(0), cse(0), cr(0), ct(0) {}
+    // first slot >= s whose segment meets the tile, with a nonzero rank
+    __device__ __forceinline__ void seek(int s) {
+        for (; s < S; ++s) {
+            const int sb = meta->indptr[s], se = meta->indptr[s + 1];
+            if (sb >= mend) {
+                s = S;
+                break;
+            }
+            const int r = meta->rank[s];
+            if (s != 0 && r != 0 && se > m0 && se > sb) {
+                csb = sb;
+                cse = se;
+                cr = r;
+                break;
+            }
+        }
+        cs = s;
+        ct = 0;
+    }
+    // the tile's first extra step: from the last slot whose segment starts at or before m0
+    __device__ __forceinline__ void start() {
+        int lo = 0, hi = S - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (meta->indptr[mid] <= m0) lo = mid;
+            else hi = mid - 1;
+        }
+        seek(lo);
+    }
+    __device__ __forceinline__ ExtraStep current() const { return ExtraStep{cs, csb, cse, cr, ct}; }
+    __device__ __forceinline__ void advance() {
+        if (++ct == spk) seek(cs + 1);
+    }
+};
+
 // Number of extra steps of `step` k (e < 0) or the decoding of step e.
 __device__ __forceinline__ int extra_steps(const MetaView& mv, const Fuse& f, int m0, int mend, int e,
                                            ExtraStep* out, int step = 64) {

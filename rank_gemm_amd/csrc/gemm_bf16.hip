@@ -145,42 +145,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     // the expand's extra steps come first: their operands (B_s rows, scaled
     // h) are cold, and the base stages that follow hide their latency
     const int ne = nt - nk;
-    // Cursor over the extra steps (slot, its segment, rank, step within the
-    // slot), advanced once per extra stage issued. The slot metadata is read
-    // from its LDS copy (the host takes this path only for pools of at most
-    // kMetaSlots slots): a flat or global load here would also wait for every
-    // direct-to-LDS load in flight.
-    auto md_indptr = [&](int i) { return meta.indptr[i]; };
-    auto md_rank = [&](int i) { return meta.rank[i]; };
-    const int spk = (2 * f.rp + BK - 1) / BK;  // extra steps per slot
-    int cs = f.S, csb = 0, cse = 0, cr = 0, ct = 0;
-    auto seek = [&](int s) {  // first slot >= s whose segment meets the tile, with a nonzero rank
-        for (; s < f.S; ++s) {
-            const int sb = md_indptr(s), se = md_indptr(s + 1);
-            if (sb >= mend) {
-                s = f.S;
-                break;
-            }
-            const int r = md_rank(s);
-            if (s != 0 && r != 0 && se > m0 && se > sb) {
-                csb = sb;
-                cse = se;
-                cr = r;
-                break;
-            }
-        }
-        cs = s;
-        ct = 0;
-    };
-    if (ne > 0) {
-        int lo = 0, hi = f.S - 1;  // last slot whose segment starts at or before m0
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (md_indptr(mid) <= m0) lo = mid;
-            else hi = mid - 1;
-        }
-        seek(lo);
-    }
+    ExtraCursor cur((lds_meta_ptr)&meta, f.S, m0, mend, (2 * f.rp + BK - 1) / BK);
+    if (ne > 0) cur.start();
     auto issue = [&](int kt) {
         u32x4* st = lds + (kt % NS) * STAGE;
         gptr<u32x4> asrc[DA], bsrc[DB];
@@ -192,8 +158,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (int b = 0; b < DB; ++b) bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
         } else {
-            const ExtraStep x{cs, csb, cse, cr, ct};
-            if (++ct == spk) seek(cs + 1);
+            const ExtraStep x = cur.current();
+            cur.advance();
             const int k = x.t * BK + cl * 8;        // position in the 2 rp extension
             const int q = k < f.rp ? k : k - f.rp;  // rank of the chunk (rp % 8 == 0)
             const bool qin = k < 2 * f.rp && q < x.r;
@@ -384,44 +350,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int ne_all = (f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0;
     const int ne = __builtin_amdgcn_readfirstlane(SPLIT ? (ne_all > kz ? (ne_all - kz + ks - 1) / ks : 0) : ne_all);
     const int nt = nk + ne;
-    // cursor over the extra steps, read from the LDS copy of the slot metadata
-    // (as in gemm_dma_kernel)
-    auto md_indptr = [&](int i) { return meta.indptr[i]; };
-    auto md_rank = [&](int i) { return meta.rank[i]; };
-    const int spk = (2 * f.rp + BK - 1) / BK;
-    int cs = f.S, csb = 0, cse = 0, cr = 0, ct = 0;
-    auto seek = [&](int s) {
-        for (; s < f.S; ++s) {
-            const int sb = md_indptr(s), se = md_indptr(s + 1);
-            if (sb >= mend) {
-                s = f.S;
-                break;
-            }
-            const int r = md_rank(s);
-            if (s != 0 && r != 0 && se > m0 && se > sb) {
-                csb = sb;
-                cse = se;
-                cr = r;
-                break;
-            }
-        }
-        cs = s;
-        ct = 0;
-    };
-    if (ne > 0) {
-        int lo = 0, hi = f.S - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (md_indptr(mid) <= m0) lo = mid;
-            else hi = mid - 1;
-        }
-        seek(lo);
-    }
-    auto advance = [&]() {
-        if (++ct == spk) seek(cs + 1);
-    };
+    ExtraCursor cur((lds_meta_ptr)&meta, f.S, m0, mend, (2 * f.rp + BK - 1) / BK);
+    if (ne > 0) cur.start();
     if constexpr (SPLIT)
-        for (int e = 0; e < kz && ne > 0; ++e) advance();  // to this split's first extra step
+        for (int e = 0; e < kz && ne > 0; ++e) cur.advance();  // to this split's first extra step
     // sources of step kt's load instructions (A 0..DA-1, then B); set once
     // per step, in step order (the cursor advances on extra steps)
     gptr<u32x4> src[ND];
@@ -441,9 +373,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         else mfma_agpr(c, w, a);
     };
     auto sources_extra = [&](int) {
-        const ExtraStep x{cs, csb, cse, cr, ct};
+        const ExtraStep x = cur.current();
 #pragma unroll 1
-        for (int e = 0; e < ks; ++e) advance();  // past the other splits' steps
+        for (int e = 0; e < ks; ++e) cur.advance();  // past the other splits' steps
         const int k = x.t * BK + cl * 8;
         const int q = k < f.rp ? k : k - f.rp;
         const bool qin = k < 2 * f.rp && q < x.r;
