@@ -567,17 +567,14 @@ GemmPlan gemm_bf16_plan(int M, int N, int K) {
     while (nsub < need && nsub < 16) nsub *= 2;
     g.nsub = nsub;
     g.ks = cdiv(K, nsub * 128);
-    // shrink splits of at least 256 k, at most 8 of them (kernel 2 adds the
-    // h planes in one round of loads)
-    g.hkc = max(256, (cdiv(K, 8) + 31) / 32 * 32);
-    g.hs = cdiv(K, g.hkc);
     return g;
 }
 
 // Workspace of the split-K pass over all slices together.
 static size_t split_workspace(int M, int n_nt_total, const GemmPlan& g, int n_slices, int r_max) {
     const size_t py = (size_t)g.ks * g.n_mt * n_nt_total * 16 * 64 * 16;
-    const size_t ph = (size_t)n_slices * g.hs * M * r_max * sizeof(float);
+    // h planes: the GEMM's ks splits (shrink tiles) or up to 8 shrink splits
+    const size_t ph = (size_t)n_slices * max(g.ks, 8) * M * r_max * sizeof(float);
     return ((py + 255) & ~size_t(255)) + ((ph + 255) & ~size_t(255));
 }
 

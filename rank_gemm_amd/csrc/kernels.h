@@ -43,7 +43,6 @@ struct GemmPlan {
     int bm, bn;          // macro tile of the tiled path
     int nsub;            // split-K path: 128-wide K sub-chunks per split (0 = tiled path)
     int ks, n_mt, n_nt;  // split-K path: splits and 64 x 64 tile grid
-    int hs, hkc;         // split-K path: shrink splits of hkc k each (hkc % 32 == 0)
     int tks, tkc;        // tiled path split over K: tks ranges of tkc k (tkc % 64 == 0); tks < 2: none
 };
 GemmPlan gemm_bf16_plan(int M, int N, int K);

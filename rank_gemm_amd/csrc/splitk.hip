@@ -5,10 +5,11 @@
 //
 // Kernel 1 computes 64 x 64 output tiles over K splits, streaming the split's
 // gathered x rows and W rows through a 5-deep LDS ring of 64-k stages by
-// direct-to-LDS loads; extra workgroups of the same launch compute the SGMV
-// shrink over the same K range in finer splits. Kernel 2 adds the partial
-// products in split order, applies the expand scale_s * h[p] B_s^T in fp32
-// and rounds once. No workgroup waits on another.
+// direct-to-LDS loads; extra tiles of the same launch compute the SGMV shrink
+// over the same K splits, with the rows of a few work items in place of the
+// batch rows and their slots' A rows in place of W rows. Kernel 2 adds the
+// partial products in split order, applies the expand scale_s * h[p] B_s^T in
+// fp32 and rounds once. No workgroup waits on another.
 //
 // Projections that read the same x (the output slices of a merged q/k/v or
 // gate/up wrapper, section "vLLM: preallocated stacked buffers plus a
@@ -17,6 +18,9 @@
 // the weight, output and adapter pool of the slice it falls in; the shrink
 // workgroups cover every slice's A over the same K splits. The MULTI template
 // flag keeps the one-slice kernels free of the slice lookup.
+#include <cstddef>
+#include <cstring>
+
 #include "fuse.h"
 #include "shrink.h"
 
@@ -25,116 +29,210 @@ namespace lora {
 // -------------------------------------------------------------- split-K --
 // The slices of one pass (projections reading the same x), their 64-column
 // tiles numbered one after the other: slice i owns tiles nt0[i] .. nt0[i+1).
+// One-slice kernels take a table of one entry: the kernel arguments stay
+// small, and their layout measurably moves the kernels' start (a table of
+// four entries made both decode kernels slower even with one slice).
+template <int NSL>
 struct SliceTable {
     int n;
-    int nt0[kMaxSlices + 1];
-    int N[kMaxSlices];
-    const uint16_t* W[kMaxSlices];
-    const uint16_t* A_pool[kMaxSlices];
-    const uint16_t* B_pool[kMaxSlices];
-    const int32_t* rank[kMaxSlices];
-    const float* scale[kMaxSlices];
-    uint16_t* Y[kMaxSlices];
+    int nt0[NSL + 1];
+    int N[NSL];
+    const uint16_t* W[NSL];
+    const uint16_t* A_pool[NSL];
+    const uint16_t* B_pool[NSL];
+    const int32_t* rank[NSL];
+    const float* scale[NSL];
+    uint16_t* Y[NSL];
 };
+using SliceTableAll = SliceTable<kMaxSlices>;
+template <bool MULTI>
+using SliceTableFor = SliceTable<MULTI ? kMaxSlices : 1>;
+
+template <int NSL>
+static SliceTable<NSL> table_of(const SliceTableAll& t) {
+    SliceTable<NSL> r{};
+    r.n = t.n;
+    for (int i = 0; i < NSL; ++i) {
+        r.nt0[i] = t.nt0[i];
+        r.N[i] = t.N[i];
+        r.W[i] = t.W[i];
+        r.A_pool[i] = t.A_pool[i];
+        r.B_pool[i] = t.B_pool[i];
+        r.rank[i] = t.rank[i];
+        r.scale[i] = t.scale[i];
+        r.Y[i] = t.Y[i];
+    }
+    r.nt0[NSL] = t.nt0[NSL];
+    return r;
+}
 
 // Entry i of a slice array, by selects (a dynamically indexed kernel
 // argument would be copied to scratch memory).
-template <class T>
-__device__ __forceinline__ T pick(const T (&v)[kMaxSlices], int i) {
+template <class T, int NSL>
+__device__ __forceinline__ T pick(const T (&v)[NSL], int i) {
     T r = v[0];
 #pragma unroll
-    for (int j = 1; j < kMaxSlices; ++j) r = i == j ? v[j] : r;
+    for (int j = 1; j < NSL; ++j) r = i == j ? v[j] : r;
     return r;
 }
 
-__device__ __forceinline__ int nt_first(const SliceTable& t, int i) {
+template <int NSL>
+__device__ __forceinline__ int nt_first(const SliceTable<NSL>& t, int i) {
     int r = t.nt0[0];
 #pragma unroll
-    for (int j = 1; j < kMaxSlices; ++j) r = i == j ? t.nt0[j] : r;
+    for (int j = 1; j < NSL; ++j) r = i == j ? t.nt0[j] : r;
     return r;
 }
 
-__device__ __forceinline__ int slice_of(const SliceTable& t, int nt) {
+template <int NSL>
+__device__ __forceinline__ int slice_of(const SliceTable<NSL>& t, int nt) {
     int i = 0;
 #pragma unroll
-    for (int j = 1; j < kMaxSlices; ++j) i += (j < t.n && nt >= t.nt0[j]) ? 1 : 0;
+    for (int j = 1; j < NSL; ++j) i += (j < t.n && nt >= t.nt0[j]) ? 1 : 0;
     return i;
 }
 
+template <int NSL>
 struct SplitArgs {
     const uint16_t* X;
     float* part_y;  // [ks][n_mt][n_nt][16 fragments][64 lanes] f32x4, n_nt over all slices
     int M, K, n_mt, n_nt, ks;
-    // shrink workgroups (the first n_items * hs * n blocks), hkc k each
+    // shrink tiles: groups of G work items, rc columns per item (r_max rounded
+    // up to 16), E 64-column tiles per group
     const int32_t* token_order;
     const Item* work;
     int n_items, r_max;
-    float* part_h;  // [n][hs][M][r_max]
+    float* part_h;  // [n][planes][M][r_max], rows by sorted position
+    // shrink workgroups (light shrinks): n_items * hs * n of them, hkc k
+    // each, hs planes; hs == 0 when the shrink runs as tiles (ks planes)
     int hs, hkc;
-    SliceTable sl;
+    int n_groups, G, rc, E;
+    SliceTable<NSL> sl;
 };
 
-// grid: n_items * hs * n shrink blocks, then n_mt * n_nt * ks GEMM blocks.
-// The shrink splits are finer than the GEMM's, so that they finish early.
-// Wave w of a GEMM block owns columns n0 + 16 w .. + 15 of a 64 x 64 tile.
-// The split's x rows (gathered through token_order) and W rows stream
-// through kSplitStages LDS buffers of 64 k by direct-to-LDS loads: a stage is
-// 8 blocks each of x and of W, a block being 8 rows x 128 B; lane i of a
-// block load fetches row i / 8, chunk (i % 8) ^ (row % 8), so that each load
+// grid: n_items * hs * n shrink workgroups (light shrinks only), then
+// n_mt * n_nt * ks GEMM blocks, then ks * n * n_groups * E shrink tiles (heavy
+// shrinks only). The shrink workgroups run shrink_item over K ranges finer
+// than the GEMM's splits, so that they finish early; a shrink tile has the
+// shape of work of a GEMM block (a 64 x 64 tile over one K split). A CU's
+// direct-to-LDS feed is the bound of this kernel: a GEMM block alone on a
+// CU streams its 256 KB in ~6.3 us, two blocks on one CU take ~10.4 us each,
+// so a few shrink tiles beside 256 GEMM blocks would set the kernel's time,
+// while many shrink tiles move fewer bytes than per-item workgroups.
+// Wave w of a block owns columns 16 w .. 16 w + 15 of its tile. The split's
+// x rows (gathered through token_order) and W rows stream through
+// kSplitStages LDS buffers of 64 k by direct-to-LDS loads: a stage is 8
+// blocks each of x and of W, a block being 8 rows x 128 B; lane i of a block
+// load fetches row i / 8, chunk (i % 8) ^ (row % 8), so that each load
 // instruction reads whole 128-byte lines and the MFMA fragment reads (row
-// l % 16, chunk l / 16) are free of bank conflicts. Rows past M or N are
-// clamped (their partials are not stored); chunks past K read zeros.
+// l % 16, chunk l / 16) are free of bank conflicts. GEMM tiles clamp rows past
+// M or N (their partials are not stored); chunks past K read zeros.
+//
+// A shrink tile of group g takes, as its row block i < G, the rows of work
+// item g G + i, and as its column c the rank q = c' % rc of item c' / rc's
+// slot (c' = 64 e + c), i.e. row q of that slot's A ("[tokens, r]-shaped in
+// the middle", opening section of "LoRA serving, embeddings, rerankers,
+// pooling", mlinterviewnotes.com). Only the blocks pairing an item's rows
+// with its own slot's ranks are kept: they are h over the split's K range,
+// written to the split's h plane. Ranks at or past r_s are never loaded
+// (rank masking, "SGLang: chunked SGMV, and a rank-aware kernel"), a row
+// block with no item issues no x loads, and a tile with no live item exits
+// before loading anything.
 constexpr int kSplitStages = 5;
 constexpr int kSplitStageChunks = 1024;  // 16-byte chunks: x 512, W 512
 
-template <int NSUB, bool MULTI>
-__global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
+template <int NSUB, bool MULTI, bool TILES>
+__global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs<MULTI ? kMaxSlices : 1> a) {
     __shared__ u32x4 lds[kSplitStages * kSplitStageChunks];  // 80 KB
     constexpr int KC = NSUB * 128, NST = NSUB * 2, NS = kSplitStages, SC = kSplitStageChunks;
-    const int n_shrink = a.n_items * a.hs * (MULTI ? a.sl.n : 1);
-    if ((int)blockIdx.x < n_shrink) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K = a.K;
+    const int n_shrink = TILES ? 0 : a.n_items * a.hs * (MULTI ? a.sl.n : 1);
+    if (!TILES && (int)blockIdx.x < n_shrink) {
         const int item = blockIdx.x % a.n_items, rest = blockIdx.x / a.n_items;
-        const int kz = MULTI ? rest % a.hs : rest, si = MULTI ? rest / a.hs : 0;
+        const int hz = MULTI ? rest % a.hs : rest, hi = MULTI ? rest / a.hs : 0;
         const Item it = a.work[item];
-        const int r = pick(a.sl.rank, si)[it.slot];
+        const int r = pick(a.sl.rank, hi)[it.slot];
         if (r == 0) return;
-        const int kbeg = kz * a.hkc, kend = min(a.K, kbeg + a.hkc);
-        const ShrinkOut out{a.part_h + ((int64_t)si * a.hs + kz) * a.M * a.r_max, nullptr, 0, 0.f};
-        shrink_item<4>(a.X, pick(a.sl.A_pool, si), r, a.token_order, it, out, a.K, kbeg, kend, a.r_max,
+        const int kbeg = hz * a.hkc, kend = min(K, kbeg + a.hkc);
+        const ShrinkOut out{a.part_h + ((int64_t)hi * a.hs + hz) * a.M * a.r_max, nullptr, 0, 0.f};
+        shrink_item<4>(a.X, pick(a.sl.A_pool, hi), r, a.token_order, it, out, K, kbeg, kend, a.r_max,
                        reinterpret_cast<f32x4*>(lds));
         return;
     }
-    const int g = blockIdx.x - n_shrink;
-    const int tiles = a.n_mt * a.n_nt;
-    const int kz = g / tiles, t = g - kz * tiles;
-    const int mt = t / a.n_nt, nt = t - mt * a.n_nt;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int si = MULTI ? slice_of(a.sl, nt) : 0;
-    const uint16_t* __restrict__ W = pick(a.sl.W, si);
-    const int N = pick(a.sl.N, si);
-    const int m0 = mt * 64, n0 = (nt - nt_first(a.sl, si)) * 64;
-    const int kbeg = kz * KC;
-    const int K = a.K;
+    const int b = blockIdx.x - n_shrink;
+    const int n_gemm = a.n_mt * a.n_nt * a.ks;
+    const bool gemm = !TILES || b < n_gemm;
     // this lane's rows and chunk in its two x and two W block loads
     const int dr = lane >> 3, dc = lane & 7;
     const uint16_t* xs[2];
     const uint16_t* ws[2];
     int kc[2];
+    bool xv[2], wv[2];
+    int kz, mt = 0, nt = 0, si = 0, g = 0, ex = 0;
+    bool xl = true;  // wave-uniform: this wave loads x rows
+    if (gemm) {
+        const int tiles = a.n_mt * a.n_nt;
+        kz = b / tiles;
+        const int t = b - kz * tiles;
+        mt = t / a.n_nt;
+        nt = t - mt * a.n_nt;
+        si = MULTI ? slice_of(a.sl, nt) : 0;
+        const uint16_t* __restrict__ W = pick(a.sl.W, si);
+        const int N = pick(a.sl.N, si);
+        const int m0 = mt * 64, n0 = (nt - nt_first(a.sl, si)) * 64;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = 16 * wave + 8 * j + dr;  // tile row / column 0..63
-        kc[j] = kbeg + (dc ^ (r & 7)) * 8;     // this lane's k within a stage
-        xs[j] = a.X + (int64_t)a.token_order[min(m0 + r, a.M - 1)] * K + kc[j];
-        ws[j] = W + (int64_t)min(n0 + r, N - 1) * K + kc[j];
+        for (int j = 0; j < 2; ++j) {
+            const int r = 16 * wave + 8 * j + dr;  // tile row / column 0..63
+            kc[j] = kz * KC + (dc ^ (r & 7)) * 8;  // this lane's k within a stage
+            xs[j] = a.X + (int64_t)a.token_order[min(m0 + r, a.M - 1)] * K + kc[j];
+            ws[j] = W + (int64_t)min(n0 + r, N - 1) * K + kc[j];
+            xv[j] = wv[j] = true;
+        }
+    } else if constexpr (TILES) {
+        int e = b - n_gemm;
+        const int ge = a.n_groups * a.E;
+        const int per_z = ge * (MULTI ? a.sl.n : 1);
+        kz = e / per_z;
+        e -= kz * per_z;
+        si = MULTI ? e / ge : 0;
+        e -= si * ge;
+        g = e / a.E;
+        ex = e - g * a.E;
+        const int32_t* rank = pick(a.sl.rank, si);
+        const uint16_t* A = pick(a.sl.A_pool, si);
+        // uniform: does a live item own columns of this tile?
+        const int j0 = 64 * ex / a.rc, j1 = min(a.G - 1, (64 * ex + 63) / a.rc);
+        bool live = false;
+        for (int j = j0; j <= j1; ++j) {
+            const int i = g * a.G + j;
+            if (i < a.n_items) {
+                const Item it = a.work[i];
+                live |= it.count > 0 && rank[it.slot] > 0;
+            }
+        }
+        if (!live) return;
+        // x rows of row block `wave`: item g G + wave
+        const int ix = g * a.G + wave;
+        const bool xin = wave < a.G && ix < a.n_items;
+        xl = xin;
+        const Item itx = a.work[xin ? ix : 0];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = 16 * wave + 8 * j + dr;
+            kc[j] = kz * KC + (dc ^ (r & 7)) * 8;
+            const int rr = 8 * j + dr;
+            xv[j] = xin && rr < itx.count;
+            xs[j] = a.X + (int64_t)a.token_order[xv[j] ? itx.begin + rr : 0] * K + kc[j];
+            // column r: rank q of item jj's slot
+            const int c = 64 * ex + r, jj = c / a.rc, q = c - jj * a.rc;
+            const int iw = g * a.G + jj;
+            const bool win = jj < a.G && iw < a.n_items;
+            const Item itw = a.work[win ? iw : 0];
+            wv[j] = win && itw.count > 0 && q < rank[itw.slot];
+            ws[j] = A + ((int64_t)(wv[j] ? itw.slot : 0) * a.r_max + (wv[j] ? q : 0)) * K + kc[j];
+        }
     }
-    auto issue = [&](int s) {
-        u32x4* st = lds + (s % NS) * SC;
-        const int k = s * 64;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dma16(or_zero(kc[j] + k < K, xs[j] + k), st + (2 * wave + j) * 64);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dma16_nt(or_zero(kc[j] + k < K, ws[j] + k), st + 512 + (2 * wave + j) * 64);
-    };
     // fragment reads: row r = lane % 16 of a 16-row tile, chunk 4 u + lane / 16
     const int fr = lane & 15, fq = lane >> 4;
     int fo[2];
@@ -143,31 +241,73 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs a) {
     f32x4 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // XL: this wave loads x rows (4 loads per stage, else 2); CHK: the loads
+    // carry the shrink tile's row and rank masks. Instantiated per case, so
+    // that the GEMM blocks' loop has no branch.
+    auto run = [&](auto xl_tag, auto chk_tag) {
+        constexpr bool XL = decltype(xl_tag)::value, CHK = decltype(chk_tag)::value;
+        auto issue = [&](int s) {
+            u32x4* st = lds + (s % NS) * SC;
+            const int k = s * 64;
+            if constexpr (XL)
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < NST) issue(s);
+                for (int j = 0; j < 2; ++j)
+                    dma16(or_zero((!CHK || xv[j]) && kc[j] + k < K, xs[j] + k), st + (2 * wave + j) * 64);
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
-        // stage s landed for this wave; the stages issued after it may be in flight
-        const int later = (s + NS - 2 < NST ? NS - 2 : NST - 1 - s);
-        static_assert(kSplitStages == 5, "wait counts assume 5 stages");
-        if (later >= 3) vm_landed<12>();
-        else if (later == 2) vm_landed<8>();
-        else if (later == 1) vm_landed<4>();
-        else vm_landed<0>();
-        stage_barrier();
-        if (s + NS - 1 < NST) issue(s + NS - 1);  // into stage s - 1's buffer
-        const u32x4* st = lds + (s % NS) * SC;
+            for (int j = 0; j < 2; ++j)
+                dma16_nt(or_zero((!CHK || wv[j]) && kc[j] + k < K, ws[j] + k), st + 512 + (2 * wave + j) * 64);
+        };
+        constexpr int PER = XL ? 4 : 2;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const u32x4 wf = st[512 + wave * 128 + fo[u]];
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < NST) issue(s);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = mfma16x16x32(st[i * 128 + fo[u]], wf, acc[i]);
+        for (int s = 0; s < NST; ++s) {
+            // stage s landed for this wave; the stages issued after it may be in flight
+            const int later = (s + NS - 2 < NST ? NS - 2 : NST - 1 - s);
+            static_assert(kSplitStages == 5, "wait counts assume 5 stages");
+            if (later >= 3) vm_landed<3 * PER>();
+            else if (later == 2) vm_landed<2 * PER>();
+            else if (later == 1) vm_landed<PER>();
+            else vm_landed<0>();
+            stage_barrier();
+            if (s + NS - 1 < NST) issue(s + NS - 1);  // into stage s - 1's buffer
+            const u32x4* st = lds + (s % NS) * SC;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const u32x4 wf = st[512 + wave * 128 + fo[u]];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = mfma16x16x32(st[i * 128 + fo[u]], wf, acc[i]);
+            }
         }
-    }
-    f32x4* out = reinterpret_cast<f32x4*>(a.part_y) + ((int64_t)(kz * a.n_mt + mt) * a.n_nt + nt) * 16 * 64;
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (!TILES || gemm) run(T_{}, F_{});
+    else if (xl) run(T_{}, T_{});
+    else run(F_{}, T_{});
+    if (!TILES || gemm) {
+        f32x4* out = reinterpret_cast<f32x4*>(a.part_y) + ((int64_t)(kz * a.n_mt + mt) * a.n_nt + nt) * 16 * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[(i * 4 + wave) * 64 + lane] = acc[i];
+        for (int i = 0; i < 4; ++i) out[(i * 4 + wave) * 64 + lane] = acc[i];
+        return;
+    }
+    // lane holds rows 4 (lane / 16) + e of every row block, column 16 wave +
+    // lane % 16; the wave's 16 columns belong to one item jj (rc % 16 == 0)
+    const int c = 64 * ex + 16 * wave + (lane & 15), jj = c / a.rc, q = c - jj * a.rc;
+    const int i = g * a.G + jj;
+    if (jj >= a.G || i >= a.n_items) return;
+    const Item it = a.work[i];
+    if (q >= pick(a.sl.rank, si)[it.slot]) return;
+    f32x4 v = acc[0];
+#pragma unroll
+    for (int b = 1; b < 4; ++b) v = jj == b ? acc[b] : v;
+    float* hp = a.part_h + ((int64_t)si * a.ks + kz) * a.M * a.r_max + (int64_t)it.begin * a.r_max + q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int rr = 4 * (lane >> 4) + e;
+        if (rr < it.count) hp[(int64_t)rr * a.r_max] = v[e];
+    }
 }
 
 // grid (n_nt, 4 * n_mt): block (nt, 4 mt + rb) finishes row block rb (16
@@ -190,7 +330,7 @@ constexpr int kLaneMetaSlots = 64;
 
 template <bool ADAPT, bool VEC, bool LANE_META, bool MULTI>
 __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* __restrict__ part_y, int ks, int n_mt,
-                                                                   int n_nt, int M, Fuse f, SliceTable tab) {
+                                                                   int n_nt, int M, Fuse f, SliceTableFor<MULTI> tab) {
     const int nt = blockIdx.x, mt = blockIdx.y >> 2, rb = blockIdx.y & 3;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int p0 = mt * 64 + rb * 16;
@@ -404,10 +544,27 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
     }
 }
 
-template <int NSUB>
-static hipError_t launch_split(const SplitArgs& a, int n_blocks, hipStream_t st, StageTimer* tm) {
-    return launch(tm, "gemm_splitk", a.sl.n > 1 ? splitk_gemm_kernel<NSUB, true> : splitk_gemm_kernel<NSUB, false>,
-                  dim3(n_blocks), dim3(kThreads), st, a);
+template <int NSUB, bool TILES>
+static hipError_t launch_split(const SplitArgs<kMaxSlices>& a, int n_blocks, hipStream_t st, StageTimer* tm) {
+    if (a.sl.n > 1)
+        return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB, true, TILES>, dim3(n_blocks), dim3(kThreads), st, a);
+    static_assert(offsetof(SplitArgs<1>, sl) == offsetof(SplitArgs<kMaxSlices>, sl), "common head");
+    SplitArgs<1> a1;
+    std::memcpy(&a1, &a, offsetof(SplitArgs<1>, sl));
+    a1.sl = table_of<1>(a.sl);
+    return launch(tm, "gemm_splitk", splitk_gemm_kernel<NSUB, false, TILES>, dim3(n_blocks), dim3(kThreads), st, a1);
+}
+
+template <bool TILES>
+static hipError_t launch_split_n(const SplitArgs<kMaxSlices>& a, int nsub, int n_blocks, hipStream_t st,
+                                 StageTimer* tm) {
+    switch (nsub) {
+        case 1: return launch_split<1, TILES>(a, n_blocks, st, tm);
+        case 2: return launch_split<2, TILES>(a, n_blocks, st, tm);
+        case 4: return launch_split<4, TILES>(a, n_blocks, st, tm);
+        case 8: return launch_split<8, TILES>(a, n_blocks, st, tm);
+        default: return launch_split<16, TILES>(a, n_blocks, st, tm);
+    }
 }
 
 template <bool MULTI>
@@ -420,7 +577,7 @@ static auto epilogue_for(const LinearArgs& L) {
 
 hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, hipStream_t st, StageTimer* tm) {
     const int M = L.M, K = L.K, n = L.n_slices;
-    SliceTable sl{};
+    SliceTableAll sl{};
     sl.n = n;
     int nt = 0;
     for (int i = 0; i < kMaxSlices; ++i) {
@@ -439,32 +596,38 @@ hipError_t splitk_forward_bf16(const LinearArgs& L, const GemmPlan& g, hipStream
     sl.nt0[kMaxSlices] = nt;
     char* ws = static_cast<char*>(L.workspace);
     const size_t py = ((size_t)g.ks * g.n_mt * nt * 16 * 64 * 16 + 255) & ~size_t(255);
-    SplitArgs a{L.X, reinterpret_cast<float*>(ws), M, K, g.n_mt, nt, g.ks, L.token_order,
-                reinterpret_cast<const Item*>(L.work), L.adapters ? L.n_items : 0, L.r_max,
-                reinterpret_cast<float*>(ws + py), g.hs, g.hkc, sl};
-    const int n_blocks = a.n_items * g.hs * n + g.n_mt * nt * g.ks;
-    hipError_t e;
-    switch (g.nsub) {
-        case 1: e = launch_split<1>(a, n_blocks, st, tm); break;
-        case 2: e = launch_split<2>(a, n_blocks, st, tm); break;
-        case 4: e = launch_split<4>(a, n_blocks, st, tm); break;
-        case 8: e = launch_split<8>(a, n_blocks, st, tm); break;
-        default: e = launch_split<16>(a, n_blocks, st, tm); break;
-    }
+    // The shrink runs as tiles when it is heavy against the GEMM (its item
+    // rows x + A_s exceed 1/8 of the GEMM tiles' x + W rows), else as
+    // workgroups over K ranges of at least 256 k, at most 8 of them. Tiles:
+    // as many items per tile as 64 columns hold whole (16-column rounded)
+    // ranks, at least one.
+    const int rc = (L.r_max + 15) & ~15, G = max(1, 64 / rc), E = cdiv(G * rc, 64);
+    const int n_items = L.adapters ? L.n_items : 0;
+    const bool tiles = (int64_t)n_items * n * (16 + rc) * 8 > (int64_t)g.n_mt * nt * 128;
+    const int hkc = max(256, (cdiv(K, 8) + 31) / 32 * 32), hs = tiles ? 0 : cdiv(K, hkc);
+    const int n_groups = tiles ? cdiv(n_items, G) : 0;
+    SplitArgs<kMaxSlices> a{L.X, reinterpret_cast<float*>(ws), M, K, g.n_mt, nt, g.ks, L.token_order,
+                reinterpret_cast<const Item*>(L.work), n_items, L.r_max,
+                reinterpret_cast<float*>(ws + py), hs, hkc, n_groups, G, rc, E, sl};
+    const int n_blocks = n_items * hs * n + g.n_mt * nt * g.ks + g.ks * n * n_groups * E;
+    const hipError_t e = tiles ? launch_split_n<true>(a, g.nsub, n_blocks, st, tm)
+                               : launch_split_n<false>(a, g.nsub, n_blocks, st, tm);
     if (e != hipSuccess) return e;
     // per-slice pool pointers and h planes are set by each kernel-2 block
-    const Fuse f{L.token_order, L.slot_indptr, a.part_h, nullptr, nullptr, nullptr, L.S, L.r_max, g.hs,
+    const Fuse f{L.token_order, L.slot_indptr, a.part_h, nullptr, nullptr, nullptr, L.S, L.r_max, tiles ? g.ks : hs,
                  (int64_t)M * L.r_max, L.adapters, nullptr, (L.r_max + 7) & ~7};
     const dim3 eg(nt, 4 * g.n_mt);
-    auto epi = n > 1 ? epilogue_for<true>(L) : epilogue_for<false>(L);
     const uint32_t shm = L.adapters ? (uint32_t)((16 * L.r_max + 32) * sizeof(float)) : 0u;
-    return launch_shm(tm, "gemm_splitk_epilogue", epi, eg, dim3(kThreads), shm, st, (const float*)a.part_y, g.ks,
-                      g.n_mt, nt, M, f, sl);
+    if (n > 1)
+        return launch_shm(tm, "gemm_splitk_epilogue", epilogue_for<true>(L), eg, dim3(kThreads), shm, st,
+                          (const float*)a.part_y, g.ks, g.n_mt, nt, M, f, sl);
+    return launch_shm(tm, "gemm_splitk_epilogue", epilogue_for<false>(L), eg, dim3(kThreads), shm, st,
+                      (const float*)a.part_y, g.ks, g.n_mt, nt, M, f, table_of<1>(sl));
 }
 
 hipError_t splitk_finish_bf16(const LinearArgs& L, const SliceArgs& s, const float* part, int ks, int n_mt,
                               const float* h, int h_splits, hipStream_t st, StageTimer* tm) {
-    SliceTable sl{};
+    SliceTable<1> sl{};
     sl.n = 1;
     sl.N[0] = s.N;
     sl.W[0] = s.W;
@@ -474,7 +637,7 @@ hipError_t splitk_finish_bf16(const LinearArgs& L, const SliceArgs& s, const flo
     sl.scale[0] = s.scale;
     sl.Y[0] = s.Y;
     const int nt = cdiv(s.N, 64);
-    for (int i = 1; i <= kMaxSlices; ++i) sl.nt0[i] = nt;
+    sl.nt0[1] = nt;
     const Fuse f{L.token_order, L.slot_indptr, h, nullptr, nullptr, nullptr, L.S, L.r_max, h_splits,
                  (int64_t)L.M * L.r_max, L.adapters, nullptr, (L.r_max + 7) & ~7};
     const dim3 eg(nt, 4 * n_mt);

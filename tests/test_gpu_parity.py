@@ -177,6 +177,8 @@ EDGE = [
     (700, 264, 4096, 4, [0, 256, 130, 17], 256, "bf16"),     # 64 x 128 tiles, 8 extension steps per slot
     (4096, 64, 4096, 4, [0, 16, 8, 4], 16, "bf16"),          # 256 x 256 tiles, a single K step
     (4096, 40, 4096, 5, [0, 16, 3, 8, 0], 16, "bf16"),       # 256 x 256 tiles, K shorter than one step
+    (96, 1032, 200, 5, [0, 32, 20, 0, 31], 32, "bf16"),      # split-K, two items per shrink tile
+    (80, 2048, 130, 4, [0, 48, 40, 33], 48, "bf16"),         # split-K, one item per shrink tile, 16 idle columns
 ]
 
 
