@@ -280,7 +280,7 @@ def main():
     k1_bytes = 2 * T * d_in + 2 * d_in * d_out + a_bytes
     k1_gbs = k1_bytes / (t1 * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("splitk_gemm_kernel<8, false>"),
+            "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("splitk_gemm_kernel<8, false, false>"),
             "kernel": "splitk_gemm_kernel (base GEMM K-split partials + SGMV shrink workgroups)",
             "bytes_per_launch": k1_bytes, "mean_us": round(t1, 3)}
     call_bytes = sb["base"] + sb["shrink"] + sb["expand"]
@@ -458,6 +458,20 @@ def main():
         for _ in range(n3):
             lora.linear(x3, W3, pool3, p3b, y=y3)
         s3b = lora.profile_end()
+        # the same product through torch's linear (hipBLASLt), against the
+        # base-only call, both timed with stream events, interleaved
+        lib_us, own_us = [], []
+        for _ in range(3):
+            for which in ("lib", "own"):
+                ev0.record()
+                for _ in range(n3):
+                    if which == "lib":
+                        torch.nn.functional.linear(x3, W3, out=y3)
+                    else:
+                        lora.linear(x3, W3, pool3, p3b, y=y3)
+                ev1.record()
+                torch.cuda.synchronize()
+                (lib_us if which == "lib" else own_us).append(ev0.elapsed_time(ev1) / n3 * 1e3)
         fl = acc.base_flops(w3.T, pr.d_in, pr.d_out)
         t_b = us_of(s3b, "gemm_bf16")
         t_f = us_of(s3, "gemm_bf16")
@@ -469,7 +483,11 @@ def main():
                    "fused_gemm_us": round(t_f, 2), "fused_frac_mfma": round(tf_f / BF16_PEAK_TFLOPS, 4),
                    "shrink_us": round(us_of(s3, "sgmv_shrink"), 2),
                    "call_ms": round(call_ms, 4), "tokens_per_s": round(w3.T / (call_ms * 1e-3), 1),
-                   "kernels": {k: round(v["mean_ms"] * 1e3, 2) for k, v in s3.items()}}
+                   "kernels": {k: round(v["mean_ms"] * 1e3, 2) for k, v in s3.items()},
+                   "vs_library": {"torch_linear_us": round(min(lib_us), 2), "base_call_us": round(min(own_us), 2),
+                                  "note": "torch.nn.functional.linear (hipBLASLt) on the same x and W against "
+                                          "lora_linear with a base-only plan; stream events over 10 calls, "
+                                          "best of 3 interleaved rounds"}}
         log(f"prefill: {prefill}")
 
     crossover = shrink_crossover(torch, np, lora) if args.crossover else None

@@ -80,6 +80,23 @@ def test_ragged_widths_and_per_slice_ranks(r_max):
     check_slices(w, ys, f"ragged r_max={r_max}")
 
 
+def test_heavy_shrink_slices_mixed_ranks():
+    """Many adapters with ranks up to 64 that differ per slice: the shrink
+    runs as shrink tiles of one item each (ranks 48 to 64 fill a tile), for
+    all three slices in the one GEMM launch."""
+    S = 21
+    g = np.random.default_rng(23)
+    ranks = [[0] + [int(v) for v in g.integers(1, 65, size=S - 1)] for _ in range(3)]
+    ranks[1][3] = 0  # a slot with no adapter in one slice only
+    alphas = [[2.0 * r for r in rr] for rr in ranks]
+    T = 200
+    ids = g.integers(0, S, size=T).astype(np.int32)
+    w = make_slices(61, T, 2056, [1024, 256, 200], S, ranks, alphas, ids, r_max=64)
+    ys, _, stats = run_multi(w, profile=True)
+    assert stats["gemm_splitk"]["count"] == 1
+    check_slices(w, ys, "heavy shrink slices")
+
+
 def test_four_slices_and_base_only_plan():
     """The maximum slice count; then a plan with no adapter row."""
     S = 5
