@@ -327,8 +327,9 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs<MULTI ?
 // LDS (one more round). Dynamic LDS: 16 * r_max + 32 floats (the tail keeps
 // the last row's 32-rank reads in bounds; what they read there is not used).
 constexpr int kLaneMetaSlots = 64;
+constexpr int kMfmaSlots = 4;  // slots of a 16-row block whose expand kernel 2 runs on the matrix cores
 
-template <bool ADAPT, bool VEC, bool LANE_META, bool MULTI>
+template <bool ADAPT, bool VEC, bool LANE_META, bool MULTI, int MQ = 0>
 __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* __restrict__ part_y, int ks, int n_mt,
                                                                    int n_nt, int M, Fuse f, SliceTableFor<MULTI> tab) {
     const int nt = blockIdx.x, mt = blockIdx.y >> 2, rb = blockIdx.y & 3;
@@ -408,8 +409,10 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
                 m_scale = f.scale;
             }
         }
-        // slots of this lane's rows
+        // slots of this lane's rows, of block row lane % 16 (row_slot) and of
+        // the block's first and last rows (its rows hold slots s_lo .. s_hi)
         int sl[4] = {0, 0, 0, 0};
+        int row_slot = 0, s_lo = 0, s_hi = 0;
         if constexpr (LANE_META) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -417,6 +420,9 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
                 const uint64_t m = __ballot(lane >= 1 && lane < S && ip <= p0 + j);
                 const int sj = p0 + j < M ? __popcll(m) : 0;
                 if ((lane >> 4) == (j >> 2)) sl[j & 3] = sj;
+                if ((lane & 15) == j) row_slot = sj;
+                if (j == 0) s_lo = sj;
+                if (p0 + j < M) s_hi = sj;
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -449,7 +455,30 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
 #pragma unroll
                 for (int c = 0; c < NC; ++c) b[e][c] = *or_zero(q0 + 8 * c < rr[e], bp[e] + q0 + 8 * c);
         };
-        if constexpr (VEC) bload(0);
+        // MQ > 0 (r_max <= 32 MQ) and at most kMfmaSlots slots in the block
+        // (uniform): the expand runs on the matrix cores, one pass per slot,
+        // D[row][col] = sum_q (scale_s h[row][q]) B_s[col][q] over the rows
+        // of slot s, the scaled h split into bf16 hi + lo (as the tiled
+        // path's extra K steps). Round 2 then loads each slot's B fragments:
+        // lane l takes column l % 16 of the wave, ranks 32 c + 8 (l / 16) ..
+        constexpr int NQ = MQ > 0 ? MQ : 1;
+        const bool mx = MQ > 0 && s_hi - s_lo < kMfmaSlots;
+        u32x4 bf[kMfmaSlots][NQ];
+        if (mx) {
+#pragma unroll
+            for (int k = 0; k < kMfmaSlots; ++k) {
+                const int sk = min(s_lo + k, S - 1);
+                const int rk_s = __shfl(rk, sk);
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    const int q0 = 32 * c + 8 * (lane >> 4);
+                    const bool ok = s_lo + k <= s_hi && sk != 0 && q0 < rk_s && n < N;
+                    bf[k][c] = *or_zero(ok, f.B_pool + ((int64_t)sk * N + min(n, N - 1)) * r_max + q0);
+                }
+            }
+        } else if constexpr (VEC) {
+            bload(0);
+        }
         issue_fence();  // round 2 is in flight
         // h planes added in split order, into LDS
         if constexpr (VEC) {
@@ -509,7 +538,45 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
                     }
             }
         };
-        if constexpr (VEC) {
+        if (mx) {
+            // h past the row's rank is not written by the shrink (stale
+            // workspace): it is dropped by a select, never multiplied
+            const float sc_row = __shfl(sv, row_slot);
+            const int rk_row = __shfl(rk, row_slot);  // every lane takes part in the shuffle
+            const int r_row = row_slot == 0 ? 0 : rk_row;
+            f32x4 dm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < kMfmaSlots; ++k) {
+                if (s_lo + k > s_hi) break;  // uniform
+                const bool mine = row_slot == s_lo + k && row_slot != 0;
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    const int q0 = 32 * c + 8 * (lane >> 4);
+                    const float* hr = hs + (lane & 15) * r_max + (q0 < r_max ? q0 : 0);
+                    const f32x4 h0 = reinterpret_cast<const f32x4*>(hr)[0];
+                    const f32x4 h1 = reinterpret_cast<const f32x4*>(hr)[1];
+                    float v[8], lo[8];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        v[t] = mine && q0 + t < r_row ? sc_row * h0[t] : 0.f;
+                        v[4 + t] = mine && q0 + 4 + t < r_row ? sc_row * h1[t] : 0.f;
+                    }
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) lo[t] = v[t] - bf16_to_f32(f32_to_bf16(v[t]));
+                    const u32x4 ahi{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                    pack_bf16x2(v[6], v[7])};
+                    const u32x4 alo{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
+                                    pack_bf16x2(lo[6], lo[7])};
+                    dm = mfma16x16x32(ahi, bf[k][c], dm);
+                    dm = mfma16x16x32(alo, bf[k][c], dm);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d[e] = dm[e];
+                sc[e] = 1.f;  // scale_s already applied
+            }
+        } else if constexpr (VEC) {
             fma_round(0);
             for (int q0 = 8 * NC; q0 < rmax; q0 += 8 * NC) {
                 bload(q0);
@@ -571,7 +638,13 @@ template <bool MULTI>
 static auto epilogue_for(const LinearArgs& L) {
     if (!L.adapters) return splitk_epilogue_kernel<false, false, false, MULTI>;
     if (L.r_max % 8 != 0) return splitk_epilogue_kernel<true, false, false, MULTI>;
-    if (L.S <= kLaneMetaSlots) return splitk_epilogue_kernel<true, true, true, MULTI>;
+    if (L.S <= kLaneMetaSlots) {
+        // the matrix-core expand for ranks up to 32 (at r_max 64 the per-lane
+        // B loads were measured faster: 12.1 against 13.0 us on a 33-slot
+        // batch of 256 rows)
+        if (L.r_max <= 32) return splitk_epilogue_kernel<true, true, true, MULTI, 1>;
+        return splitk_epilogue_kernel<true, true, true, MULTI>;
+    }
     return splitk_epilogue_kernel<true, true, false, MULTI>;
 }
 
