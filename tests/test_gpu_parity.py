@@ -201,6 +201,26 @@ def test_edge_shapes(case):
     check_close(to_f64(y), ref, dtype, f"edge {EDGE[case]}", base)
 
 
+@pytest.mark.parametrize("r_max", [16, 32])
+def test_block_starting_on_base_rows(r_max):
+    """A 16-row block of the decode path whose first rows (in plan order) are
+    on slot 0 and the rest on adapter slots: the slot ids' lanes of that block
+    hold base rows. Regression case for a rank taken through a shuffle that
+    only the adapter rows' lanes executed (a shuffle reads 0 from an inactive
+    lane), which dropped those rows' correction."""
+    S = 6
+    ranks = [0, 8, r_max, 12, r_max, 3]
+    alphas = [2.0 * r for r in ranks]
+    # plan order: 6 rows of slot 0, 10 of slot 2, 3 of slot 3, 13 of slot 4, 16 of slot 5
+    ids = np.array([0] * 6 + [2] * 10 + [3] * 3 + [4] * 13 + [5] * 16, np.int32)
+    ids = ids[np.random.default_rng(5).permutation(len(ids))]
+    w = make_custom(77 + r_max, len(ids), 1024, 256, S, ranks, alphas, ids, r_max=r_max)
+    proj = w.projections[0]
+    y, _, _ = run_layer(w, proj)
+    ref, base = oracle_pair(w, proj)
+    check_close(to_f64(y), ref, w.dtype, f"block on base rows r_max={r_max}", base)
+
+
 @pytest.mark.parametrize("S,r_max,split", [(9, 16, True), (70, 8, False), (9, 5, False)])
 def test_tiled_split_over_k(S, r_max, split):
     """Mid-sized T with a long K runs the 256 x 128 tiled kernel split over K
