@@ -351,9 +351,13 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
     // splits are added in split order; loads are issued unconditionally from
     // clamped addresses (a load under a branch is waited on inside it) and
     // the extra ones are not added
-    f32x4 part[8];
+    f32x4 part[8] = {};
 #pragma unroll
-    for (int z = 0; z < 8; ++z) part[z] = in[min(z, ks - 1) * zstride + o];
+    for (int z = 0; z < 4; ++z) part[z] = in[min(z, ks - 1) * zstride + o];
+    if (ks > 4) {  // uniform
+#pragma unroll
+        for (int z = 4; z < 8; ++z) part[z] = in[min(z, ks - 1) * zstride + o];
+    }
     int tok[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) tok[e] = f.token_order[min(p0 + (lane >> 4) * 4 + e, M - 1)];
