@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
             sv = f.scale[min(lane, S - 1)];
         }
         // h: 16 rows x r_max, h_splits planes; 16-byte pieces when VEC
-        constexpr int HU = 2;  // pieces per thread in round 1
+        constexpr int HU = MQ == 1 ? 1 : 2;  // pieces per thread in round 1 (r_max <= 32: 16 r_max / 4 <= 256)
         const int rq = VEC ? r_max >> 2 : r_max;
         const int npc = 16 * rq;
         f32x4 hv[HU][8];
