@@ -26,8 +26,13 @@
  *    mlinterviewnotes.com).
  *  - Element type is the pool's: LORA_BF16 (uint16 bf16 bit patterns,
  *    fp32 accumulation, y rounded to nearest even) or LORA_F32.
- *  - Widths: d_in must be a multiple of 8; d_out, T and S are otherwise
- *    free (ragged tails are masked).
+ *  - Widths are free: T, d_in, d_out and S take any value in range, and
+ *    ragged tails are masked (the page's kernels "mask odd widths": section
+ *    "Many adapters, one base-model batch"). bf16 pools whose d_in is a
+ *    multiple of 8 run the matrix-core kernels, whose rows are read in
+ *    16-byte pieces; fp32 pools and bf16 pools of any other d_in run the
+ *    element-generic kernels (scalar loads, fp32 FMA, the expand fused into
+ *    the base GEMM's epilogue, one rounding of y).
  */
 #ifndef RANK_GEMM_AMD_LORA_H
 #define RANK_GEMM_AMD_LORA_H
@@ -82,8 +87,8 @@ typedef struct lora_plan_info {
  *   scale_dev dev float [S]          alpha_s / r_s per slot, 0 for empty
  * Slot 0 stays rank 0, scale 0 for the pool's lifetime.
  * Synchronises `stream`. Errors: LORA_EINVAL (S < 2, r_max outside
- * [1, LORA_MAX_RANK], d_in < 8 or not a multiple of 8, d_out < 1, unknown
- * dtype, null pointer), LORA_EHIP.
+ * [1, LORA_MAX_RANK], d_in < 1, d_out < 1, unknown dtype, null pointer),
+ * LORA_EHIP.
  */
 int lora_pool_create(lora_pool** out, int S, int r_max, int d_in, int d_out, int dtype,
                      void* A_pool, void* B_pool, int32_t* rank_dev, float* scale_dev, void* stream);
@@ -272,8 +277,8 @@ int lora_shrink(const lora_pool* pool, const void* x, const int32_t* token_order
  * per item of up to 16 tokens.
  *   slot_ids  dev int32 [T]; ids outside [1, S) give zero rows
  *   workspace dev, at least lora_workspace_bytes(pool, T) bytes
- * bf16 pools only. Errors: LORA_EINVAL (fp32 pool, null pointer), LORA_ESPACE,
- * LORA_EHIP.
+ * bf16 pools whose d_in is a multiple of 8 only. Errors: LORA_EINVAL (fp32
+ * pool, d_in % 8 != 0, null pointer), LORA_ESPACE, LORA_EHIP.
  */
 int lora_shrink_bgmv(const lora_pool* pool, const void* x, const int32_t* slot_ids, int T, float* h,
                      void* workspace, size_t workspace_bytes, void* stream);

@@ -89,7 +89,10 @@ static void slot_offsets(int S, const int32_t* rank, int d_in, int d_out, int64_
  * Per-row unmerged formula. Computes the requested rows (rows == NULL: all
  * T rows in order) into y_out[n][d_out]. If h_out is not NULL it also
  * receives h_i[q] = sum_k x[i,k] A_s[q,k] for q < rank[s] (zeros elsewhere
- * and for rows on slot 0), with row stride h_stride.
+ * and for rows on slot 0), with row stride h_stride. If base_out is not
+ * NULL it also receives the base term sum_k W[j,k] x[i,k] of every element,
+ * the same value y_out starts from, so a caller that needs both the layer
+ * and the base output pays for one pass over W.
  * Returns 0, or -1 for a slot id outside [0, S).
  */
 int oracle_lora_rows(int dtype, int T, int d_in, int d_out, int S,
@@ -98,7 +101,7 @@ int oracle_lora_rows(int dtype, int T, int d_in, int d_out, int S,
                      const void* A_cat, const void* B_cat,
                      const int32_t* slot_ids,
                      int n_rows, const int32_t* rows,
-                     double* y_out, double* h_out, int h_stride) {
+                     double* y_out, double* h_out, int h_stride, double* base_out) {
     int64_t* a_off = (int64_t*)malloc(sizeof(int64_t) * S);
     int64_t* b_off = (int64_t*)malloc(sizeof(int64_t) * S);
     slot_offsets(S, rank, d_in, d_out, a_off, b_off);
@@ -141,6 +144,7 @@ int oracle_lora_rows(int dtype, int T, int d_in, int d_out, int S,
                 y = base + scale * e;
             }
             y_out[(int64_t)n_i * d_out + j] = y;
+            if (base_out) base_out[(int64_t)n_i * d_out + j] = base;
         }
         if (h_out) {
             double* hr = h_out + (int64_t)n_i * h_stride;

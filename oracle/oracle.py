@@ -44,7 +44,7 @@ def _load():
                 build(force=True)
             lib = ctypes.CDLL(_LIB)
             sig = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
-            lib.oracle_lora_rows.argtypes = sig + [_I, _P, _P, _P, _I]
+            lib.oracle_lora_rows.argtypes = sig + [_I, _P, _P, _P, _I, _P]
             lib.oracle_lora_rows.restype = _I
             lib.oracle_lora_merged.argtypes = sig + [_P]
             lib.oracle_lora_merged.restype = _I
@@ -112,10 +112,12 @@ def _args(dtype, x, W, S, adapters, slot_ids):
     return head, keep, T, d_out, int(rank.max(initial=0))
 
 
-def lora_rows(dtype, x, W, S, adapters, slot_ids, rows=None, want_h=False, h_width=None):
-    """fp64 y for the requested rows (all rows if None); optionally h.
+def lora_rows(dtype, x, W, S, adapters, slot_ids, rows=None, want_h=False, h_width=None, want_base=False):
+    """fp64 y for the requested rows (all rows if None); optionally h and the
+    base term x W^T of the same rows (from the same pass over W).
 
-    Returns y [n, d_out] (and h [n, h_width] if want_h)."""
+    Returns y [n, d_out], then h [n, h_width] if want_h, then base [n, d_out]
+    if want_base (a tuple when either is asked for)."""
     head, keep, T, d_out, rmax = _args(dtype, x, W, S, adapters, slot_ids)
     if rows is None:
         rows_arr, n, rows_p = None, T, None
@@ -125,11 +127,14 @@ def lora_rows(dtype, x, W, S, adapters, slot_ids, rows=None, want_h=False, h_wid
     y = np.empty((n, d_out), np.float64)
     hw = int(h_width if h_width is not None else max(rmax, 1))
     h = np.empty((n, hw), np.float64) if want_h else None
-    rc = _load().oracle_lora_rows(*head, n, rows_p, _ptr(y), _ptr(h) if want_h else None, hw)
+    base = np.empty((n, d_out), np.float64) if want_base else None
+    rc = _load().oracle_lora_rows(*head, n, rows_p, _ptr(y), _ptr(h) if want_h else None, hw,
+                                  _ptr(base) if want_base else None)
     if rc != 0:
         raise ValueError("oracle: slot id or row index out of range")
     del keep, rows_arr
-    return (y, h) if want_h else y
+    out = (y,) + ((h,) if want_h else ()) + ((base,) if want_base else ())
+    return out if len(out) > 1 else y
 
 
 def lora_merged(dtype, x, W, S, adapters, slot_ids):

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "liblora.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "pool.hip", "gemm_bf16.hip", "splitk.hip", "gemm_f32.hip", "sgmv.hip",
+SOURCES = ["api.cpp", "plan.cpp", "pool.hip", "gemm_bf16.hip", "splitk.hip", "generic.hip", "sgmv.hip",
            "plan_device.hip"]
 
 # Packed fp32 instructions are kept out of every kernel (-packed-fp32-ops).

@@ -33,6 +33,11 @@ inline size_t es_of(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// The vector kernels read rows of x, W and A_s in 16-byte pieces: bf16 pools
+// whose d_in is a multiple of 8. Every other pool (fp32, or rows that do not
+// start on 16-byte boundaries) takes the element-generic kernels.
+inline bool vector_path(const lora_pool* p) { return p->dtype == LORA_BF16 && p->d_in % 8 == 0; }
+
 // K splits of the stand-alone shrinks: SGMV over few items (at most
 // kShrinkSplitMaxBlocks workgroups) and BGMV (one workgroup per token and split)
 inline void sgmv_split(int n_items, int K, int* hs, int* hkc) {
@@ -53,7 +58,7 @@ inline void bgmv_split(int T, int K, int* hs, int* hkc) {
 // shrinks' h plus split planes; the fp32 path's h
 inline size_t h_bytes(const lora_pool* p, int T) {
     const size_t h = align256((size_t)T * p->r_max * sizeof(float));
-    if (p->dtype != LORA_BF16) return h;
+    if (!vector_path(p)) return h;
     const size_t g = lora::gemm_bf16_workspace(T, &p->d_out, 1, p->d_in, p->r_max);
     const size_t rows = std::max<size_t>({(size_t)lora::kShrinkSplitMaxBlocks * 16, 2048, (size_t)T});
     const size_t s = h + align256(rows * p->r_max * sizeof(float));
@@ -85,7 +90,7 @@ int check_slices(const lora_slice* sl, int n, const void* x, bool buffers) {
 size_t multi_bytes(const lora_slice* sl, int n, int T) {
     const lora_pool* p0 = sl[0].pool;
     const size_t h = align256((size_t)T * p0->r_max * sizeof(float));
-    if (p0->dtype != LORA_BF16) return h;
+    if (!vector_path(p0)) return h;
     int N[LORA_MAX_SLICES];
     for (int i = 0; i < n; ++i) N[i] = sl[i].pool->d_out;
     const size_t g = lora::gemm_bf16_workspace(T, N, n, p0->d_in, p0->r_max);
@@ -172,7 +177,7 @@ int lora_pool_create(lora_pool** out, int S, int r_max, int d_in, int d_out, int
                      int32_t* rank_dev, float* scale_dev, void* stream) {
     if (!out) return LORA_EINVAL;
     *out = nullptr;
-    if (S < 2 || r_max < 1 || r_max > LORA_MAX_RANK || d_in < 8 || d_in % 8 != 0 || d_out < 1) return LORA_EINVAL;
+    if (S < 2 || r_max < 1 || r_max > LORA_MAX_RANK || d_in < 1 || d_out < 1) return LORA_EINVAL;
     if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_EINVAL;
     if (!A_pool || !B_pool || !rank_dev || !scale_dev) return LORA_EINVAL;
     lora_pool* p = new (std::nothrow) lora_pool();
@@ -276,7 +281,7 @@ int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t*
     if (profiler().on) lk.lock();
     lora::StageTimer* tm = timer_for(st);
 
-    if (p->dtype == LORA_BF16) {
+    if (vector_path(p)) {
         if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
         lora::LinearArgs la{};
         la.X = (const uint16_t*)x;
@@ -295,16 +300,13 @@ int lora_linear(const lora_pool* p, const void* x, const void* W, const int32_t*
                        p->rank_dev, p->scale_dev};
         return lora::lora_forward_bf16(la, st, tm) == hipSuccess ? LORA_OK : LORA_EHIP;
     }
-    if (lora::gemm_f32((const float*)x, (const float*)W, (float*)y, T, p->d_out, p->d_in, st, tm) != hipSuccess)
-        return LORA_EHIP;
-    if (!adapters) return LORA_OK;  // no adapter row: y is the base output
-    if (lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, h, p->d_in, p->r_max, st,
-                          tm) != hipSuccess)
-        return LORA_EHIP;
-    if (lora::sgmv_expand_f32(h, (const float*)p->B, p->rank_dev, p->scale_dev, token_order, work, info->n_items,
-                              (float*)y, p->d_out, p->r_max, st, tm) != hipSuccess)
-        return LORA_EHIP;
-    return LORA_OK;
+    // element-generic kernels: the shrink (adapter rows only), then the base
+    // GEMM with the expand in its epilogue
+    return lora::generic_linear(p->dtype, x, W, y, token_order, slot_indptr, work, info->n_items, p->S, p->A, p->B,
+                                p->rank_dev, p->scale_dev, h, adapters ? 1 : 0, T, p->d_out, p->d_in, p->r_max, st,
+                                tm) == hipSuccess
+               ? LORA_OK
+               : LORA_EHIP;
 }
 
 size_t lora_plan_device_words(int T, int S) {
@@ -362,9 +364,9 @@ int lora_linear_multi(const lora_slice* slices, int n, const void* x, const int3
     const int T = info->T;
     if (T == 0) return LORA_OK;
     if (!x) return LORA_EINVAL;
-    if (p0->dtype != LORA_BF16) {
-        // fp32 pools: the slices one after another on the same stream (the
-        // workspace is reused in stream order)
+    if (!vector_path(p0)) {
+        // element-generic pools: the slices one after another on the same
+        // stream (the workspace is reused in stream order)
         for (int i = 0; i < n; ++i) {
             rc = lora_linear(slices[i].pool, x, slices[i].W, token_order, slot_indptr, work, info, slices[i].y,
                              workspace, workspace_bytes, stream);
@@ -414,14 +416,19 @@ int lora_shrink(const lora_pool* p, const void* x, const int32_t* token_order, c
     if (profiler().on) lk.lock();
     lora::StageTimer* tm = timer_for(st);
     int ks = 1, kc = p->d_in;
-    if (p->dtype == LORA_BF16) sgmv_split(info->n_items, p->d_in, &ks, &kc);
+    if (vector_path(p)) sgmv_split(info->n_items, p->d_in, &ks, &kc);
     if (info->n_items > 0) {
-        const hipError_t e =
-            ks > 1 ? lora::sgmv_shrink_split((const uint16_t*)x, (const uint16_t*)p->A, p->rank_dev, p->scale_dev,
-                                             token_order, work, info->n_items, ks, kc, part, hs, nullptr, p->d_in,
-                                             p->r_max, st, tm)
-                   : lora::sgmv_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, hs, p->d_in,
-                                       p->r_max, st, tm);
+        hipError_t e;
+        if (!vector_path(p))
+            e = lora::generic_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, hs, p->d_in,
+                                     p->r_max, st, tm);
+        else if (ks > 1)
+            e = lora::sgmv_shrink_split((const uint16_t*)x, (const uint16_t*)p->A, p->rank_dev, p->scale_dev,
+                                        token_order, work, info->n_items, ks, kc, part, hs, nullptr, p->d_in,
+                                        p->r_max, st, tm);
+        else
+            e = lora::sgmv_shrink((const uint16_t*)x, (const uint16_t*)p->A, p->rank_dev, token_order, work,
+                                  info->n_items, hs, p->d_in, p->r_max, st, tm);
         if (e != hipSuccess) return LORA_EHIP;
     }
     if (lora::scatter_h(hs, p->rank_dev, token_order, slot_indptr, p->S, h, T, p->r_max, st, tm) != hipSuccess)
@@ -432,7 +439,7 @@ int lora_shrink(const lora_pool* p, const void* x, const int32_t* token_order, c
 int lora_shrink_bgmv(const lora_pool* p, const void* x, const int32_t* slot_ids, int T, float* h, void* workspace,
                      size_t workspace_bytes, void* stream) {
     if (!p || T < 0) return LORA_EINVAL;
-    if (p->dtype != LORA_BF16) return LORA_EINVAL;
+    if (!vector_path(p)) return LORA_EINVAL;
     if (T == 0) return LORA_OK;
     if (!x || !slot_ids || !h) return LORA_EINVAL;
     if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;

@@ -679,7 +679,7 @@ static hipError_t tiled_shrink(const LinearArgs& L, const SliceArgs& sl, char* w
     float* part = reinterpret_cast<float*>(ws + ((h_final + 255) & ~size_t(255)));
     return hs > 1 ? sgmv_shrink_split(L.X, sl.A_pool, sl.rank, sl.scale, L.token_order, L.work, L.n_items, hs, hkc,
                                       part, h, ext, K, L.r_max, st, tm)
-                  : sgmv_shrink(1, L.X, sl.A_pool, sl.rank, L.token_order, L.work, L.n_items, h, K, L.r_max, st, tm,
+                  : sgmv_shrink(L.X, sl.A_pool, sl.rank, L.token_order, L.work, L.n_items, h, K, L.r_max, st, tm,
                                 sl.scale, ext);
 }
 

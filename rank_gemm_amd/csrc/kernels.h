@@ -74,7 +74,18 @@ struct LinearArgs {
 // workspace of a forward over slices of N[0..n_slices) columns
 size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max);
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm);
-hipError_t gemm_f32(const float* X, const float* W, float* Y, int M, int N, int K, hipStream_t st, StageTimer* tm);
+
+// ---- element-generic path (fp32 pools; bf16 pools with d_in % 8 != 0) --------
+// dtype 0 = fp32, 1 = bf16. Shrink into h [T][r_max] fp32 (sorted positions),
+// then the base GEMM over sorted positions with the expand in its epilogue and
+// one rounding; with adapters == 0 neither h nor the pool is read.
+hipError_t generic_shrink(int dtype, const void* X, const void* A_pool, const int32_t* rank,
+                          const int32_t* token_order, const int32_t* work, int n_items, float* h, int K, int r_max,
+                          hipStream_t st, StageTimer* tm);
+hipError_t generic_linear(int dtype, const void* X, const void* W, void* Y, const int32_t* token_order,
+                          const int32_t* slot_indptr, const int32_t* work, int n_items, int S, const void* A_pool,
+                          const void* B_pool, const int32_t* rank, const float* scale, float* h, int adapters, int M,
+                          int N, int K, int r_max, hipStream_t st, StageTimer* tm);
 
 // ---- device planner -----------------------------------------------------------
 // plan: [work 4 * cap][token_order T][slot_indptr S + 1][info 8], work padded
@@ -82,11 +93,11 @@ hipError_t gemm_f32(const float* X, const float* W, float* Y, int M, int N, int 
 constexpr int kDevPlanMaxSlots = 4096;
 hipError_t plan_device(const int32_t* ids, int T, int S, int cap, int32_t* plan, hipStream_t st);
 
-// ---- SGMV shrink and the fp32 expand -----------------------------------------
+// ---- SGMV shrink (bf16, K % 8 == 0) --------------------------------------------
 // h: fp32 [T][r_max] indexed by sorted position (rows of adapter items only).
-// With ext (bf16 pools only), writes the expand operand of the tiled GEMM's
-// extra K steps, scale_s * h as bf16 hi / lo: [T][2][round_up(r_max, 8)].
-hipError_t sgmv_shrink(int dtype, const void* X, const void* A_pool, const int32_t* rank,
+// With ext, writes the expand operand of the tiled GEMM's extra K steps,
+// scale_s * h as bf16 hi / lo: [T][2][round_up(r_max, 8)].
+hipError_t sgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank,
                        const int32_t* token_order, const int32_t* work, int n_items, float* h, int K, int r_max,
                        hipStream_t st, StageTimer* tm, const float* scale = nullptr, uint16_t* ext = nullptr);
 // The same over hs K ranges of hkc k each (few items, long K): fp32 planes in
@@ -101,9 +112,6 @@ hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const in
 hipError_t bgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* slot_ids,
                        int S, int T, int hs, int hkc, float* part, float* h, int K, int r_max, hipStream_t st,
                        StageTimer* tm);
-hipError_t sgmv_expand_f32(const float* h, const float* B_pool, const int32_t* rank, const float* scale,
-                           const int32_t* token_order, const int32_t* work, int n_items, float* Y, int N, int r_max,
-                           hipStream_t st, StageTimer* tm);
 hipError_t scatter_h(const float* h, const int32_t* rank, const int32_t* token_order, const int32_t* slot_indptr,
                      int S, float* h_out, int T, int r_max, hipStream_t st, StageTimer* tm);
 

@@ -1,5 +1,6 @@
-// Segmented gather shrink (SGMV) of the LoRA correction on gfx950, and the
-// fp32-pool expand.
+// Segmented gather shrink (SGMV) of the LoRA correction on gfx950 (bf16
+// pools with 16-byte aligned rows), its BGMV counterpart and the scatter of h
+// to token order.
 //
 // The plan groups tokens by slot ("LoRA serving, embeddings, rerankers,
 // pooling", mlinterviewnotes.com, section "vLLM: preallocated stacked
@@ -147,51 +148,6 @@ __global__ __launch_bounds__(256) void bgmv_finish_kernel(const float* __restric
     h[i] = v;
 }
 
-// fp32 pools: one thread per (row, rank), plain fp32 FMA over K.
-__global__ __launch_bounds__(256) void shrink_f32_kernel(const float* __restrict__ X, const float* __restrict__ A_pool,
-                                                         const int32_t* __restrict__ rank,
-                                                         const int32_t* __restrict__ token_order,
-                                                         const Item* __restrict__ work, float* __restrict__ h, int K,
-                                                         int r_max) {
-    const Item it = work[blockIdx.x];
-    const int r = rank[it.slot];
-    if (r == 0) return;
-    const int m = threadIdx.x >> 4;
-    if (m >= it.count) return;
-    const float* xp = X + (int64_t)token_order[it.begin + m] * K;
-    float* hp = h + (int64_t)(it.begin + m) * r_max;
-    for (int q = threadIdx.x & 15; q < r; q += 16) {
-        const float* ap = A_pool + ((int64_t)it.slot * r_max + q) * K;
-        float s = 0.f;
-        for (int k = 0; k < K; ++k) s = __builtin_fmaf(xp[k], ap[k], s);
-        hp[q] = s;
-    }
-}
-
-// fp32 pools: y[t_p][j] += scale_s * sum_q h[p][q] * B_s[j][q], one thread
-// per output column, the item's rows in turn.
-__global__ __launch_bounds__(256) void expand_f32_kernel(const float* __restrict__ h, const float* __restrict__ B_pool,
-                                                         const int32_t* __restrict__ rank,
-                                                         const float* __restrict__ scale,
-                                                         const int32_t* __restrict__ token_order,
-                                                         const Item* __restrict__ work, float* __restrict__ Y, int N,
-                                                         int r_max) {
-    const Item it = work[blockIdx.x];
-    const int r = rank[it.slot];
-    if (r == 0) return;
-    const int j = blockIdx.y * 256 + threadIdx.x;
-    if (j >= N) return;
-    const float sc = scale[it.slot];
-    const float* bp = B_pool + ((int64_t)it.slot * N + j) * r_max;
-    for (int m = 0; m < it.count; ++m) {
-        const float* hp = h + (int64_t)(it.begin + m) * r_max;
-        float e = 0.f;
-        for (int q = 0; q < r; ++q) e = __builtin_fmaf(bp[q], hp[q], e);
-        float* yp = Y + (int64_t)token_order[it.begin + m] * N + j;
-        *yp = __builtin_fmaf(sc, e, *yp);
-    }
-}
-
 // h_out[t][q] (token order) from h[p][q] (sorted order); zeros for slot 0,
 // rank-0 slots and q >= r_s.
 __global__ __launch_bounds__(256) void scatter_h_kernel(const float* __restrict__ h, const int32_t* __restrict__ rank,
@@ -211,20 +167,15 @@ __global__ __launch_bounds__(256) void scatter_h_kernel(const float* __restrict_
     h_out[(int64_t)token_order[p] * r_max + q] = v;
 }
 
-hipError_t sgmv_shrink(int dtype, const void* X, const void* A_pool, const int32_t* rank, const int32_t* token_order,
+hipError_t sgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* token_order,
                        const int32_t* work, int n_items, float* h, int K, int r_max, hipStream_t st,
                        StageTimer* tm, const float* scale, uint16_t* ext) {
     if (n_items == 0) return hipSuccess;
-    if (dtype == 1) {
-        if (n_items >= 256)
-            return launch(tm, "sgmv_shrink", shrink_bf16_kernel<4>, dim3(n_items), dim3(256), st,
-                          (const uint16_t*)X, (const uint16_t*)A_pool, rank, scale, token_order, (const Item*)work, h,
-                          ext, K, r_max);
-        return launch(tm, "sgmv_shrink", shrink_bf16_kernel<16>, dim3(n_items), dim3(1024), st, (const uint16_t*)X,
-                      (const uint16_t*)A_pool, rank, scale, token_order, (const Item*)work, h, ext, K, r_max);
-    }
-    return launch(tm, "sgmv_shrink", shrink_f32_kernel, dim3(n_items), dim3(256), st, (const float*)X,
-                  (const float*)A_pool, rank, token_order, (const Item*)work, h, K, r_max);
+    if (n_items >= 256)
+        return launch(tm, "sgmv_shrink", shrink_bf16_kernel<4>, dim3(n_items), dim3(256), st, X, A_pool, rank, scale,
+                      token_order, (const Item*)work, h, ext, K, r_max);
+    return launch(tm, "sgmv_shrink", shrink_bf16_kernel<16>, dim3(n_items), dim3(1024), st, X, A_pool, rank, scale,
+                  token_order, (const Item*)work, h, ext, K, r_max);
 }
 
 hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const float* scale,
@@ -249,14 +200,6 @@ hipError_t bgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t*
     const int64_t n = (int64_t)T * r_max;
     return launch(tm, "bgmv_finish", bgmv_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,
                   (const float*)part, rank, slot_ids, S, h, T, hs, r_max);
-}
-
-hipError_t sgmv_expand_f32(const float* h, const float* B_pool, const int32_t* rank, const float* scale,
-                           const int32_t* token_order, const int32_t* work, int n_items, float* Y, int N, int r_max,
-                           hipStream_t st, StageTimer* tm) {
-    if (n_items == 0) return hipSuccess;
-    return launch(tm, "sgmv_expand", expand_f32_kernel, dim3(n_items, (N + 255) / 256), dim3(256), st, h, B_pool,
-                  rank, scale, token_order, (const Item*)work, Y, N, r_max);
 }
 
 hipError_t scatter_h(const float* h, const int32_t* rank, const int32_t* token_order, const int32_t* slot_indptr,

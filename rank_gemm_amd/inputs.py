@@ -146,7 +146,8 @@ CONFIG_NAMES = {
     1: "tiny fp32: T=64, 256->256, S=5 (rank 8, alpha 16), uniform slots",
     2: "llama3-8b q_proj decode bf16: T=64, 4096->4096, S=9 (rank 16, alpha 32), 8 adapters x 8 tokens shuffled",
     3: "llama3-8b gate/up prefill bf16: T=8192 (16 seqs x 512), 4096->14336 x2, S=17 (rank 16, alpha 32)",
-    4: "llama3-8b k/v mixed ranks bf16: T=256, 4096->1024, S=33 (ranks {8,16,32,64}, r_max 64, alpha 2r), Zipf(1.1), 20% base rows",
+    4: "llama3-8b k/v mixed ranks bf16: T=256, 4096->1024 x2 (k_proj, v_proj on one x), S=33 (ranks {8,16,32,64}, "
+       "r_max 64, alpha 2r), Zipf(1.1), 20% base rows",
     5: "llama3-8b o_proj + down_proj bf16: T=512, 4096->4096 and 14336->4096, S=129 (rank 16, alpha 32), 50 active adapters",
 }
 
@@ -194,8 +195,9 @@ def make_config(i: int, seed: int | None = None, layer: int = 0, pool=None) -> W
             base_pos = g.choice(T, size=n_base, replace=False)
             rest = np.setdiff1d(np.arange(T), base_pos)
             slot_ids[rest] = _zipf_slots(g, len(rest), S - 1, 1.1)
-            projs = [_projection(wseed, 0, "k_proj", T, 4096, 1024, dt, ranks, alphas, pool=pool)]
-            return Workload(CONFIG_NAMES[4], dt, T, S, r_max, slot_ids, projs)
+            k = _projection(wseed, 0, "k_proj", T, 4096, 1024, dt, ranks, alphas, pool=pool)
+            v = _projection(wseed, 1, "v_proj", T, 4096, 1024, dt, ranks, alphas, x=k.x, pool=pool)
+            return Workload(CONFIG_NAMES[4], dt, T, S, r_max, slot_ids, [k, v])
         if i == 5:
             T, S, r, dt = 512, 129, 16, BF16
             ranks = np.array([0] + [r] * (S - 1), np.int32)

@@ -40,9 +40,10 @@ def oracle_rows(w, proj, rows=None, slot_ids=None, want_h=False):
 
 
 def oracle_pair(w, proj, rows=None, slot_ids=None):
-    """(y_ref, base_ref): the oracle's output and its base-only output."""
+    """(y_ref, base_ref): the oracle's output and its base-only output x W^T,
+    both from one pass of the oracle over W."""
     ids = w.slot_ids if slot_ids is None else slot_ids
-    return oracle_rows(w, proj, rows, ids), oracle_rows(w, proj, rows, np.zeros_like(ids))
+    return oracle.lora_rows(w.dtype, proj.x, proj.W, w.S, proj.adapters, ids, rows=rows, want_base=True)
 
 
 def rel_err(y, ref):

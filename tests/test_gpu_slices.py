@@ -138,6 +138,18 @@ def test_f32_slices():
     check_slices(w, ys, "f32 slices")
 
 
+def test_unaligned_width_slices():
+    """bf16 pools with d_in % 8 != 0 run the element-generic kernels slice
+    after slice."""
+    S = 4
+    ranks = [[0, 8, 5, 8], [0, 3, 0, 8]]
+    alphas = [[2.0 * r for r in rk] for rk in ranks]
+    ids = np.random.default_rng(9).integers(0, S, size=90).astype(np.int32)
+    w = make_slices(62, 90, 515, [200, 72], S, ranks, alphas, ids, r_max=8)
+    ys, _, _ = run_multi(w)
+    check_slices(w, ys, "unaligned slices")
+
+
 def test_multi_argument_errors():
     """Pools that cannot share a call, aliasing outputs and a short workspace
     are refused before any launch."""

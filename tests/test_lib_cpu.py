@@ -131,7 +131,7 @@ def test_host_argument_errors():
     # invalid shapes are refused before any HIP call
     assert L.lora_pool_create(ctypes.byref(h), 1, 16, 64, 64, 1, 1, 1, 1, 1, None) == lora.LORA_EINVAL
     assert L.lora_pool_create(ctypes.byref(h), 4, 0, 64, 64, 1, 1, 1, 1, 1, None) == lora.LORA_EINVAL
-    assert L.lora_pool_create(ctypes.byref(h), 4, 16, 60, 64, 1, 1, 1, 1, 1, None) == lora.LORA_EINVAL
+    assert L.lora_pool_create(ctypes.byref(h), 4, 16, 0, 64, 1, 1, 1, 1, 1, None) == lora.LORA_EINVAL
     assert L.lora_pool_create(ctypes.byref(h), 4, 16, 64, 0, 1, 1, 1, 1, 1, None) == lora.LORA_EINVAL
     assert L.lora_pool_create(ctypes.byref(h), 4, 16, 64, 64, 7, 1, 1, 1, 1, None) == lora.LORA_EINVAL
     assert L.lora_pool_create(ctypes.byref(h), 4, 16, 64, 64, 1, None, 1, 1, 1, None) == lora.LORA_EINVAL

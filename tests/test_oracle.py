@@ -145,6 +145,25 @@ def test_slot0_rows_are_exact_base(dtype):
     assert np.all(np.abs(y[~base_rows] - y0[~base_rows]).max(axis=1) > 0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_base_output_equals_all_slot0_run(dtype):
+    """The base term returned beside y (want_base) is, bit for bit, the y of a
+    run where every row is on slot 0, and it equals numpy's x W^T within
+    rounding; y itself is unchanged by asking for it."""
+    S, ranks = 4, [0, 2, 3, 1]
+    x, W, ads, slot_ids = random_case(15, 33, 16, 12, S, ranks, dtype, p0=0.3)
+    y_alone = oracle.lora_rows(dtype, x, W, S, ads, slot_ids)
+    y, base = oracle.lora_rows(dtype, x, W, S, ads, slot_ids, want_base=True)
+    np.testing.assert_array_equal(y, y_alone)
+    np.testing.assert_array_equal(base, oracle.lora_rows(dtype, x, W, S, ads, np.zeros_like(slot_ids)))
+    np.testing.assert_allclose(base, as_f64(x, dtype) @ as_f64(W, dtype).T, rtol=1e-13, atol=1e-13)
+    rows = np.array([0, 5, 32, 7], np.int32)
+    y_r, h_r, base_r = oracle.lora_rows(dtype, x, W, S, ads, slot_ids, rows=rows, want_h=True, h_width=3,
+                                        want_base=True)
+    np.testing.assert_array_equal(y_r, y[rows])
+    np.testing.assert_array_equal(base_r, base[rows])
+
+
 def test_rank1_closed_form():
     """A rank-1 adapter adds scale * (a . x) * b, an outer product."""
     x, W, _, _ = random_case(7, 9, 10, 6, 2, [0, 1], "f32")
