@@ -73,6 +73,8 @@ typedef struct lora_plan_info {
     int32_t k;       /* distinct non-zero slots that have tokens */
     int32_t n_items; /* entries in the work list */
     int32_t max_seg; /* longest non-zero segment, in tokens */
+    int32_t chunk;   /* rows per work item at most: LORA_PLAN_ROWS, or the
+                        chunk of lora_plan_chunked */
 } lora_plan_info;
 
 /*
@@ -143,8 +145,25 @@ int lora_pool_rank(const lora_pool* pool, int slot);
 int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_order, int32_t* slot_indptr,
               int32_t* work, int work_cap, lora_plan_info* info);
 
-/* Upper bound on the work list length of any plan over T tokens, S slots. */
+/* Upper bound on the work list length of any plan over T tokens, S slots
+ * (of any chunk: larger chunks give fewer items). */
 int lora_plan_max_items(int T, int S);
+
+/*
+ * lora_plan with work items of up to `chunk` rows, chunk in {16, 32, 64,
+ * 128}: the chunked SGMV of "LoRA serving, embeddings, rerankers, pooling"
+ * (mlinterviewnotes.com), section "SGLang: chunked SGMV, and a rank-aware
+ * kernel", where the chunk size trades parallelism on skewed adapter
+ * popularity (more, shorter items for a hot adapter) against re-reading the
+ * adapter's weights once per item. token_order and slot_indptr do not depend
+ * on the chunk; info->chunk records it. lora_plan is this call with
+ * chunk = LORA_PLAN_ROWS. lora_linear, lora_linear_multi and lora_shrink
+ * take plans of LORA_PLAN_ROWS rows only (their kernels are built on 16-row
+ * items); lora_delta takes any chunk. Errors as lora_plan, plus LORA_EINVAL
+ * for another chunk.
+ */
+int lora_plan_chunked(int S, const int32_t* slot_ids, int T, int chunk, int32_t* token_order,
+                      int32_t* slot_indptr, int32_t* work, int work_cap, lora_plan_info* info);
 
 /*
  * The same plan built on the device, for steps captured in a HIP graph (no
@@ -282,6 +301,44 @@ int lora_shrink(const lora_pool* pool, const void* x, const int32_t* token_order
  */
 int lora_shrink_bgmv(const lora_pool* pool, const void* x, const int32_t* slot_ids, int T, float* h,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The correction alone, for callers that compute the base product
+ * themselves: y += delta(x), the LoraLayerDelta contract of
+ * "mstar.engine.resources.lora.pool" (mstar.stanford.edu):
+ *   y[t][n] = round(y[t][n] + (alpha_s / r_s) sum_q h[t][q] B_s[n][q]),
+ *   h[t][q] = sum_k x[t][k] A_s[q][k]
+ * for every token t whose slot s is >= 1 with r_s > 0; other rows of y are
+ * not touched. fp32 accumulation, one rounding of each updated element (so a
+ * bf16 y that already held a rounded base output is rounded twice in all).
+ *   x            dev [T][d_in], y dev [T][d_out] (in place; must not alias x)
+ *   token_order, slot_indptr, work, info: a plan of any chunk (lora_plan or
+ *                lora_plan_chunked), on the device as for lora_linear
+ *   workspace    dev, at least lora_workspace_bytes(pool, T) bytes
+ * SGMV form: per work item, its rows of x are shrunk against A_s (read once
+ * per item), then B_s is read once per item and column block and applied to
+ * every row of the item. Asynchronous on `stream`. Errors: LORA_EINVAL
+ * (null pointer, plan/pool mismatch, a chunk outside {16, 32, 64, 128}),
+ * LORA_ESPACE, LORA_EHIP.
+ */
+int lora_delta(const lora_pool* pool, const void* x, const int32_t* token_order, const int32_t* slot_indptr,
+               const int32_t* work, const lora_plan_info* info, void* y, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * The same correction in BGMV form: token by token from the raw slot map,
+ * with no grouping and no plan; each token reads its own slot's A_s and B_s
+ * (the batched gather matrix-vector kernel that "43. Beyond text: images,
+ * embeddings, reranking and many LoRAs" (inference.shantanugoel.com), section
+ * "Many adapters, one base-model batch", uses for both the shrink and the
+ * expand).
+ *   slot_ids  dev int32 [T]; ids outside [1, S) and rank-0 slots leave their
+ *             row of y unchanged
+ * bf16 pools whose d_in is a multiple of 8 only. Errors: LORA_EINVAL (other
+ * pools, null pointer, y aliasing x), LORA_ESPACE, LORA_EHIP.
+ */
+int lora_delta_bgmv(const lora_pool* pool, const void* x, const int32_t* slot_ids, int T, void* y, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * Per-kernel timing, for diagnostics and the benchmark's roofline figures.

@@ -66,6 +66,7 @@ inline size_t h_bytes(const lora_pool* p, int T) {
 }
 
 static_assert(LORA_MAX_SLICES == lora::kMaxSlices, "slice limit of the interface and the kernels");
+static_assert(LORA_MAX_RANK == lora::kMaxRank, "rank limit of the interface and the kernels");
 
 // Every slice's pool must agree with the first on S, r_max, d_in and element
 // type; with buffers, no output may alias x, a weight or another output.
@@ -146,11 +147,16 @@ lora::StageTimer* timer_for(hipStream_t st) {
     return &p;
 }
 
+inline bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+
+// A plan for this pool; `any_chunk` admits plans of chunked items (lora_delta),
+// every other caller needs LORA_PLAN_ROWS-row items.
 int check_plan(const lora_pool* p, const int32_t* token_order, const int32_t* slot_indptr, const int32_t* work,
-               const lora_plan_info* info) {
+               const lora_plan_info* info, bool any_chunk = false) {
     if (!p || !info) return LORA_EINVAL;
     if (info->S != p->S || info->T < 0 || info->T_a < 0 || info->T_a > info->T || info->n_items < 0)
         return LORA_EINVAL;
+    if (any_chunk ? !valid_chunk(info->chunk) : info->chunk != LORA_PLAN_ROWS) return LORA_EINVAL;
     if (info->T > 0 && (!token_order || !slot_indptr)) return LORA_EINVAL;
     if (info->n_items > 0 && !work) return LORA_EINVAL;
     return LORA_OK;
@@ -330,7 +336,7 @@ int lora_linear_device_plan(const lora_pool* p, const void* x, const void* W, co
     const int32_t* slot_indptr = token_order + T;
     // the host knows only the shapes: every row may carry an adapter, and the
     // work list is launched at its capacity (padding items are on slot 0)
-    lora_plan_info info{T, p->S, T, 0, lora_plan_max_items(T, p->S), 0};
+    lora_plan_info info{T, p->S, T, 0, lora_plan_max_items(T, p->S), 0, LORA_PLAN_ROWS};
     return lora_linear(p, x, W, token_order, slot_indptr, work, &info, y, workspace, workspace_bytes, stream);
 }
 
@@ -344,7 +350,7 @@ int lora_linear_multi_device_plan(const lora_slice* slices, int n, const void* x
     const int32_t* work = plan;
     const int32_t* token_order = plan + 4 * (size_t)cap;
     const int32_t* slot_indptr = token_order + T;
-    lora_plan_info info{T, p0->S, T, 0, lora_plan_max_items(T, p0->S), 0};
+    lora_plan_info info{T, p0->S, T, 0, lora_plan_max_items(T, p0->S), 0, LORA_PLAN_ROWS};
     return lora_linear_multi(slices, n, x, token_order, slot_indptr, work, &info, workspace, workspace_bytes, stream);
 }
 
@@ -452,6 +458,65 @@ int lora_shrink_bgmv(const lora_pool* p, const void* x, const int32_t* slot_ids,
     lora::StageTimer* tm = timer_for(st);
     return lora::bgmv_shrink((const uint16_t*)x, (const uint16_t*)p->A, p->rank_dev, slot_ids, p->S, T, ks, kc, part,
                              h, p->d_in, p->r_max, st, tm) == hipSuccess
+               ? LORA_OK
+               : LORA_EHIP;
+}
+
+int lora_delta(const lora_pool* p, const void* x, const int32_t* token_order, const int32_t* slot_indptr,
+               const int32_t* work, const lora_plan_info* info, void* y, void* workspace, size_t workspace_bytes,
+               void* stream) {
+    int rc = check_plan(p, token_order, slot_indptr, work, info, true);
+    if (rc != LORA_OK) return rc;
+    const int T = info->T;
+    if (T == 0) return LORA_OK;
+    if (!x || !y || y == x) return LORA_EINVAL;
+    if (info->T_a == 0 || info->n_items == 0) return LORA_OK;
+    if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
+    hipStream_t st = as_stream(stream);
+    std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
+    if (profiler().on) lk.lock();
+    lora::StageTimer* tm = timer_for(st);
+    float* part = static_cast<float*>(workspace);
+    hipError_t e;
+    if (vector_path(p)) {
+        // split K over workgroups when the items are few; the planes
+        // [hs][T][r_max] fit the workspace while hs <= 1 + max(4096, T) / T
+        int hs = 1, hkc = p->d_in;
+        sgmv_split(info->n_items, p->d_in, &hs, &hkc);
+        const int cap = 1 + std::max(4096, T) / T;
+        if (hs > cap) {
+            hkc = std::max(256, ((p->d_in + cap - 1) / cap + 31) / 32 * 32);
+            hs = (p->d_in + hkc - 1) / hkc;
+        }
+        e = lora::delta_sgmv((const uint16_t*)x, (const uint16_t*)p->A, (const uint16_t*)p->B, p->rank_dev,
+                             p->scale_dev, token_order, work, info->n_items, info->chunk, hs, hkc, part, (uint16_t*)y,
+                             T, p->d_out, p->d_in, p->r_max, st, tm);
+    } else {
+        e = lora::generic_shrink(p->dtype, x, p->A, p->rank_dev, token_order, work, info->n_items, part, p->d_in,
+                                 p->r_max, st, tm);
+        if (e == hipSuccess)
+            e = lora::generic_expand(p->dtype, part, p->B, p->rank_dev, p->scale_dev, token_order, work,
+                                     info->n_items, y, p->d_out, p->r_max, st, tm);
+    }
+    return e == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+int lora_delta_bgmv(const lora_pool* p, const void* x, const int32_t* slot_ids, int T, void* y, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!p || T < 0) return LORA_EINVAL;
+    if (!vector_path(p)) return LORA_EINVAL;
+    if (T == 0) return LORA_OK;
+    if (!x || !slot_ids || !y || y == x) return LORA_EINVAL;
+    if (!workspace || workspace_bytes < lora_workspace_bytes(p, T)) return LORA_ESPACE;
+    hipStream_t st = as_stream(stream);
+    int hs = 1, hkc = p->d_in;
+    bgmv_split(T, p->d_in, &hs, &hkc);
+    std::unique_lock<std::mutex> lk(profiler().mu, std::defer_lock);
+    if (profiler().on) lk.lock();
+    lora::StageTimer* tm = timer_for(st);
+    return lora::delta_bgmv((const uint16_t*)x, (const uint16_t*)p->A, (const uint16_t*)p->B, p->rank_dev,
+                            p->scale_dev, slot_ids, p->S, hs, hkc, static_cast<float*>(workspace), (uint16_t*)y, T,
+                            p->d_out, p->d_in, p->r_max, st, tm) == hipSuccess
                ? LORA_OK
                : LORA_EHIP;
 }

@@ -43,8 +43,8 @@ __device__ __forceinline__ uint16_t st_elem<uint16_t>(float v) {
     return f32_to_bf16(v);
 }
 
-// grid n_items, 256 threads: thread (m = tid / 16, q0 = tid % 16) computes
-// rows m of the item and ranks q0, q0 + 16, ... below r_s.
+// grid n_items, 256 threads: thread (m0 = tid / 16, q0 = tid % 16) computes
+// rows m0, m0 + 16, ... of the item and ranks q0, q0 + 16, ... below r_s.
 template <typename E>
 __global__ __launch_bounds__(256) void shrink_generic_kernel(const E* __restrict__ X, const E* __restrict__ A_pool,
                                                              const int32_t* __restrict__ rank,
@@ -54,15 +54,41 @@ __global__ __launch_bounds__(256) void shrink_generic_kernel(const E* __restrict
     const Item it = work[blockIdx.x];
     const int r = rank[it.slot];
     if (r == 0) return;
-    const int m = threadIdx.x >> 4;
-    if (m >= it.count) return;
-    const int64_t xrow = (int64_t)token_order[it.begin + m] * K;
-    float* hp = h + (int64_t)(it.begin + m) * r_max;
-    for (int q = threadIdx.x & 15; q < r; q += 16) {
-        const int64_t arow = ((int64_t)it.slot * r_max + q) * K;
-        float s = 0.f;
-        for (int k = 0; k < K; ++k) s = __builtin_fmaf(ld_elem(X, xrow + k), ld_elem(A_pool, arow + k), s);
-        hp[q] = s;
+    for (int m = threadIdx.x >> 4; m < it.count; m += 16) {
+        const int64_t xrow = (int64_t)token_order[it.begin + m] * K;
+        float* hp = h + (int64_t)(it.begin + m) * r_max;
+        for (int q = threadIdx.x & 15; q < r; q += 16) {
+            const int64_t arow = ((int64_t)it.slot * r_max + q) * K;
+            float s = 0.f;
+            for (int k = 0; k < K; ++k) s = __builtin_fmaf(ld_elem(X, xrow + k), ld_elem(A_pool, arow + k), s);
+            hp[q] = s;
+        }
+    }
+}
+
+// y[t_p][n] = round(y[t_p][n] + scale_s * sum_q h[p][q] B_s[n][q]) in place,
+// one thread per output column, the item's rows in turn (items of any row
+// count). grid (n_items, ceil(N / 256)).
+template <typename E>
+__global__ __launch_bounds__(256) void expand_generic_kernel(const float* __restrict__ h, const E* __restrict__ B_pool,
+                                                             const int32_t* __restrict__ rank,
+                                                             const float* __restrict__ scale,
+                                                             const int32_t* __restrict__ token_order,
+                                                             const Item* __restrict__ work, E* __restrict__ Y, int N,
+                                                             int r_max) {
+    const Item it = work[blockIdx.x];
+    const int r = rank[it.slot];
+    if (r == 0) return;
+    const int n = blockIdx.y * 256 + threadIdx.x;
+    if (n >= N) return;
+    const float sc = scale[it.slot];
+    const E* bp = B_pool + ((int64_t)it.slot * N + n) * r_max;
+    for (int m = 0; m < it.count; ++m) {
+        const float* hp = h + (int64_t)(it.begin + m) * r_max;
+        float e = 0.f;
+        for (int q = 0; q < r; ++q) e = __builtin_fmaf(ld_elem(bp, q), hp[q], e);
+        E* yp = Y + (int64_t)token_order[it.begin + m] * N + n;
+        *yp = st_elem<E>(__builtin_fmaf(sc, e, ld_elem(yp, 0)));
     }
 }
 
@@ -156,6 +182,18 @@ hipError_t generic_shrink(int dtype, const void* X, const void* A_pool, const in
                       (const uint16_t*)X, (const uint16_t*)A_pool, rank, token_order, (const Item*)work, h, K, r_max);
     return launch(tm, "sgmv_shrink", shrink_generic_kernel<float>, dim3(n_items), dim3(256), st, (const float*)X,
                   (const float*)A_pool, rank, token_order, (const Item*)work, h, K, r_max);
+}
+
+hipError_t generic_expand(int dtype, const float* h, const void* B_pool, const int32_t* rank, const float* scale,
+                          const int32_t* token_order, const int32_t* work, int n_items, void* Y, int N, int r_max,
+                          hipStream_t st, StageTimer* tm) {
+    if (n_items == 0 || N == 0) return hipSuccess;
+    const dim3 grid(n_items, (N + 255) / 256);
+    if (dtype == 1)
+        return launch(tm, "delta_expand", expand_generic_kernel<uint16_t>, grid, dim3(256), st, h,
+                      (const uint16_t*)B_pool, rank, scale, token_order, (const Item*)work, (uint16_t*)Y, N, r_max);
+    return launch(tm, "delta_expand", expand_generic_kernel<float>, grid, dim3(256), st, h, (const float*)B_pool, rank,
+                  scale, token_order, (const Item*)work, (float*)Y, N, r_max);
 }
 
 hipError_t generic_linear(int dtype, const void* X, const void* W, void* Y, const int32_t* token_order,

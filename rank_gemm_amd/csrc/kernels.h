@@ -107,13 +107,35 @@ hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const in
                              const int32_t* token_order, const int32_t* work, int n_items, int hs, int hkc,
                              float* part, float* h, uint16_t* ext, int K, int r_max, hipStream_t st,
                              StageTimer* tm);
-// BGMV shrink (token by token, no plan): planes part [hs][T][r_max], then h
-// [T][r_max] in token order.
+// BGMV shrink (token by token, no plan): planes part [hs][T][r_max] (q < r_s
+// of tokens on an installed slot only), then h [T][r_max] in token order.
+hipError_t bgmv_shrink_planes(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* slot_ids,
+                              int S, int T, int hs, int hkc, float* part, int K, int r_max, hipStream_t st,
+                              StageTimer* tm);
 hipError_t bgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* slot_ids,
                        int S, int T, int hs, int hkc, float* part, float* h, int K, int r_max, hipStream_t st,
                        StageTimer* tm);
 hipError_t scatter_h(const float* h, const int32_t* rank, const int32_t* token_order, const int32_t* slot_indptr,
                      int S, float* h_out, int T, int r_max, hipStream_t st, StageTimer* tm);
+
+// ---- the correction alone, y += delta (bf16, K % 8 == 0) --------------------------
+// SGMV over a plan of `chunk`-row items (16, 32, 64, 128): shrink into planes
+// part [hs][T][r_max] by sorted position over hs K ranges of hkc k, then the
+// expand adds the planes and updates y in place. BGMV: the same token by token
+// from device slot ids, planes by token index.
+constexpr int kMaxRank = 1024;
+hipError_t delta_sgmv(const uint16_t* X, const uint16_t* A_pool, const uint16_t* B_pool, const int32_t* rank,
+                      const float* scale, const int32_t* token_order, const int32_t* work, int n_items, int chunk,
+                      int hs, int hkc, float* part, uint16_t* Y, int T, int N, int K, int r_max, hipStream_t st,
+                      StageTimer* tm);
+hipError_t delta_bgmv(const uint16_t* X, const uint16_t* A_pool, const uint16_t* B_pool, const int32_t* rank,
+                      const float* scale, const int32_t* slot_ids, int S, int hs, int hkc, float* part, uint16_t* Y,
+                      int T, int N, int K, int r_max, hipStream_t st, StageTimer* tm);
+// element-generic pools: h from generic_shrink (items of any row count), then
+// y[t_p][n] = round(y + scale_s * h[p] . B_s[n]) in place
+hipError_t generic_expand(int dtype, const float* h, const void* B_pool, const int32_t* rank, const float* scale,
+                          const int32_t* token_order, const int32_t* work, int n_items, void* Y, int N, int r_max,
+                          hipStream_t st, StageTimer* tm);
 
 // ---- slot pool ------------------------------------------------------------
 hipError_t pool_check_finite(int dtype, const void* p, int64_t n, int* flag, hipStream_t st);

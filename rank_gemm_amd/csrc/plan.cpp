@@ -18,9 +18,10 @@ extern "C" int lora_plan_max_items(int T, int S) {
     return T / LORA_PLAN_ROWS + segs;
 }
 
-extern "C" int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_order, int32_t* slot_indptr,
-                         int32_t* work, int work_cap, lora_plan_info* info) {
+extern "C" int lora_plan_chunked(int S, const int32_t* slot_ids, int T, int chunk, int32_t* token_order,
+                                 int32_t* slot_indptr, int32_t* work, int work_cap, lora_plan_info* info) {
     if (S < 1 || T < 0 || !slot_indptr || !info || (T > 0 && (!slot_ids || !token_order))) return LORA_EINVAL;
+    if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return LORA_EINVAL;
     for (int t = 0; t < T; ++t)
         if (slot_ids[t] < 0 || slot_ids[t] >= S) return LORA_ESLOT;
 
@@ -30,7 +31,7 @@ extern "C" int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_o
     for (int s = 1; s < S; ++s) {
         if (count[s] == 0) continue;
         ++k;
-        n_items += (count[s] + LORA_PLAN_ROWS - 1) / LORA_PLAN_ROWS;
+        n_items += (count[s] + chunk - 1) / chunk;
         if (count[s] > max_seg) max_seg = count[s];
     }
     if (n_items > 0 && (!work || work_cap < n_items)) return LORA_ESPACE;
@@ -44,11 +45,11 @@ extern "C" int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_o
 
     int i = 0;
     for (int s = 1; s < S; ++s)
-        for (int p = slot_indptr[s]; p < slot_indptr[s + 1]; p += LORA_PLAN_ROWS) {
+        for (int p = slot_indptr[s]; p < slot_indptr[s + 1]; p += chunk) {
             const int left = slot_indptr[s + 1] - p;
             work[4 * i + 0] = s;
             work[4 * i + 1] = p;
-            work[4 * i + 2] = left < LORA_PLAN_ROWS ? left : LORA_PLAN_ROWS;
+            work[4 * i + 2] = left < chunk ? left : chunk;
             work[4 * i + 3] = 0;
             ++i;
         }
@@ -58,5 +59,11 @@ extern "C" int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_o
     info->k = k;
     info->n_items = n_items;
     info->max_seg = max_seg;
+    info->chunk = chunk;
     return LORA_OK;
+}
+
+extern "C" int lora_plan(int S, const int32_t* slot_ids, int T, int32_t* token_order, int32_t* slot_indptr,
+                         int32_t* work, int work_cap, lora_plan_info* info) {
+    return lora_plan_chunked(S, slot_ids, T, LORA_PLAN_ROWS, token_order, slot_indptr, work, work_cap, info);
 }

@@ -190,12 +190,19 @@ hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const in
                   rank, scale, (const Item*)work, h, ext, n_items, hs, r_max);
 }
 
+hipError_t bgmv_shrink_planes(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* slot_ids,
+                              int S, int T, int hs, int hkc, float* part, int K, int r_max, hipStream_t st,
+                              StageTimer* tm) {
+    if (T == 0) return hipSuccess;
+    return launch(tm, "bgmv_shrink", bgmv_shrink_kernel, dim3(T, hs), dim3(256), st, X, A_pool, rank, slot_ids, S,
+                  part, T, hkc, K, r_max);
+}
+
 hipError_t bgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const int32_t* slot_ids,
                        int S, int T, int hs, int hkc, float* part, float* h, int K, int r_max, hipStream_t st,
                        StageTimer* tm) {
     if (T == 0) return hipSuccess;
-    hipError_t e = launch(tm, "bgmv_shrink", bgmv_shrink_kernel, dim3(T, hs), dim3(256), st, X, A_pool, rank,
-                          slot_ids, S, part, T, hkc, K, r_max);
+    hipError_t e = bgmv_shrink_planes(X, A_pool, rank, slot_ids, S, T, hs, hkc, part, K, r_max, st, tm);
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)T * r_max;
     return launch(tm, "bgmv_finish", bgmv_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st,

@@ -30,7 +30,7 @@ EXPORTS = (
     "lora_plan", "lora_plan_max_items", "lora_workspace_bytes", "lora_linear", "lora_shrink",
     "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_workspace_bytes_multi",
     "lora_linear_multi", "lora_plan_device_words", "lora_plan_device", "lora_linear_device_plan",
-    "lora_shrink_bgmv", "lora_linear_multi_device_plan",
+    "lora_shrink_bgmv", "lora_linear_multi_device_plan", "lora_plan_chunked", "lora_delta", "lora_delta_bgmv",
 )
 LORA_DEVICE_PLAN_MAX_SLOTS = 4096
 LORA_MAX_SLICES = 4
@@ -47,7 +47,7 @@ class LoraError(RuntimeError):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("S", ctypes.c_int32), ("T_a", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("n_items", ctypes.c_int32), ("max_seg", ctypes.c_int32)]
+                ("n_items", ctypes.c_int32), ("max_seg", ctypes.c_int32), ("chunk", ctypes.c_int32)]
 
 
 class SliceDesc(ctypes.Structure):
@@ -81,6 +81,9 @@ def lib():
             L.lora_pool_rank.argtypes = [_P, _I]
             L.lora_plan.argtypes = [_I, _P, _I, _P, _P, _P, _I, ctypes.POINTER(PlanInfo)]
             L.lora_plan_max_items.argtypes = [_I, _I]
+            L.lora_plan_chunked.argtypes = [_I, _P, _I, _I, _P, _P, _P, _I, ctypes.POINTER(PlanInfo)]
+            L.lora_delta.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
+            L.lora_delta_bgmv.argtypes = [_P, _P, _P, _I, _P, _P, _SZ, _P]
             L.lora_workspace_bytes.argtypes = [_P, _I]
             L.lora_workspace_bytes.restype = _SZ
             L.lora_linear.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
@@ -162,7 +165,8 @@ class Pool:
                                           self.B.data_ptr(), self.rank_dev.data_ptr(), self.scale_dev.data_ptr(),
                                           _stream(self.device)), "lora_pool_create")
         self._h = h
-        self._ws = None
+        self._ws = {}  # stream handle -> workspace
+        self._ws_retired = []
 
     @property
     def handle(self):
@@ -191,10 +195,20 @@ class Pool:
         return int(lib().lora_workspace_bytes(self._h, int(T)))
 
     def workspace(self, T: int) -> torch.Tensor:
+        """A device workspace of at least workspace_bytes(T) for calls on the
+        current stream. One buffer per stream, so calls on two streams never
+        share one; calls on one stream reuse it in stream order. A buffer
+        that grows is replaced, but the old one is kept until the pool is
+        released (a captured graph or a call still in flight may use it)."""
         n = self.workspace_bytes(T)
-        if self._ws is None or self._ws.numel() < n:
-            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
-        return self._ws
+        key = torch.cuda.current_stream(self.device).cuda_stream
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < n:
+            if ws is not None:
+                self._ws_retired.append(ws)
+            ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -206,11 +220,12 @@ class Pool:
 class Plan:
     """Host result of lora_plan plus its device copy."""
 
-    def __init__(self, S, T, info, host, dev, n_work):
-        self.S, self.T, self.info = S, T, info
+    def __init__(self, S, T, info, host, dev, n_work, chunk=LORA_PLAN_ROWS):
+        self.S, self.T, self.info, self.chunk = S, T, info, chunk
         self.host = host  # pinned int32: [work 4*n_work][token_order T][slot_indptr S+1]
         self.dev = dev
         self._n_work = n_work
+        self._stage, self._ev, self._turn = [None, None], [None, None], 0  # plan_into staging
 
     def _off(self, which):
         if which == "work":
@@ -238,9 +253,12 @@ class Plan:
         return (base + 4 * self._off("token_order"), base + 4 * self._off("slot_indptr"), base + 4 * self._off("work"))
 
 
-def plan(slot_ids, S: int, device="cuda", upload: bool = True) -> Plan:
-    """lora_plan over host slot ids; with ``upload`` the result is copied to
-    ``device`` on the current stream (non-blocking, from pinned memory)."""
+def plan(slot_ids, S: int, device="cuda", upload: bool = True, chunk: int = LORA_PLAN_ROWS) -> Plan:
+    """lora_plan (or lora_plan_chunked for ``chunk`` of 32, 64 or 128 rows
+    per work item) over host slot ids; with ``upload`` the result is copied
+    to ``device`` on the current stream (non-blocking, from pinned memory).
+    lora_linear, lora_linear_multi and lora_shrink take 16-row plans only;
+    lora_delta takes any chunk."""
     ids = np.ascontiguousarray(np.asarray(slot_ids), dtype=np.int32)
     if ids.ndim != 1:
         raise ValueError("slot_ids must be 1-D")
@@ -251,28 +269,50 @@ def plan(slot_ids, S: int, device="cuda", upload: bool = True) -> Plan:
     host = torch.empty(total, dtype=torch.int32, pin_memory=pin)
     base = host.data_ptr()
     info = PlanInfo()
-    _check(lib().lora_plan(int(S), ids.ctypes.data, T, base + 16 * n_work, base + 4 * (4 * n_work + T), base,
-                           n_work, ctypes.byref(info)), "lora_plan")
+    _check(lib().lora_plan_chunked(int(S), ids.ctypes.data, T, int(chunk), base + 16 * n_work,
+                                   base + 4 * (4 * n_work + T), base, n_work, ctypes.byref(info)),
+           "lora_plan_chunked")
     dev = None
     if upload:
         _require_gpu()
         dev = torch.empty(total, dtype=torch.int32, device=device)
         dev.copy_(host, non_blocking=True)
-    return Plan(int(S), T, info, host, dev, n_work)
+    return Plan(int(S), T, info, host, dev, n_work, int(chunk))
 
 
 def plan_into(p: Plan, slot_ids) -> Plan:
     """Re-plan ``slot_ids`` into the device buffer of an existing plan (same
-    T and S), so work captured against that buffer sees the new plan. The
-    summary (p.info) is refreshed; kernels captured with an older summary
-    stay valid only while it is unchanged, which the caller checks."""
-    q = plan(slot_ids, p.S, upload=False)
-    if q.T != p.T or q._n_work != p._n_work:
+    T and S, same chunk), so work captured against that buffer sees the new
+    plan. The summary (p.info) is refreshed; kernels captured with an older
+    summary stay valid only while it is unchanged, which the caller checks.
+
+    The plan is written into one of two pinned staging buffers that the plan
+    owns for its lifetime, in turn, and copied from there on the current
+    stream. Before a staging buffer is written again, the host waits for the
+    copy that last read it (two plans back). No pinned memory is allocated
+    per call: registering new host memory with the GPU stalls the kernels
+    running at that moment."""
+    ids = np.ascontiguousarray(np.asarray(slot_ids), dtype=np.int32)
+    if ids.ndim != 1 or ids.shape[0] != p.T:
         raise ValueError("plan_into needs the same T and S")
-    host = torch.empty(q.host.numel(), dtype=torch.int32, pin_memory=True)
-    host.copy_(q.host)
+    if p.dev is None:
+        raise ValueError("plan was not uploaded")
+    k = p._turn
+    p._turn ^= 1
+    if p._stage[k] is None:
+        p._stage[k] = torch.empty(p.host.numel(), dtype=torch.int32, pin_memory=True)
+        p._ev[k] = torch.cuda.Event()
+    else:
+        p._ev[k].synchronize()
+    host = p._stage[k]
+    base = host.data_ptr()
+    info = PlanInfo()
+    _check(lib().lora_plan_chunked(int(p.S), ids.ctypes.data, p.T, p.chunk, base + 16 * p._n_work,
+                                   base + 4 * (4 * p._n_work + p.T), base, p._n_work, ctypes.byref(info)),
+           "lora_plan_chunked")
     p.dev.copy_(host, non_blocking=True)
-    p.host, p.info = host, q.info
+    p._ev[k].record()
+    p.host, p.info = host, info
     return p
 
 
@@ -423,6 +463,37 @@ def shrink_bgmv(x: torch.Tensor, pool: Pool, slot_ids: torch.Tensor, h: torch.Te
     _check(lib().lora_shrink_bgmv(pool.handle, x.data_ptr(), slot_ids.data_ptr(), T, h.data_ptr(), ws.data_ptr(),
                                   ws.numel() * ws.element_size(), _stream(x.device)), "lora_shrink_bgmv")
     return h
+
+
+def correction(x: torch.Tensor, pool: Pool, p: Plan, y: torch.Tensor,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """lora_delta: y += per-row adapter correction (SGMV over a plan of any
+    chunk); rows on slot 0 are not touched."""
+    tdt = _TORCH_DTYPE[pool.dtype]
+    _dev_tensor(x, tdt, "x", (p.T, pool.d_in))
+    _dev_tensor(y, tdt, "y", (p.T, pool.d_out))
+    if p.dev is None:
+        raise ValueError("plan was not uploaded")
+    ws = workspace if workspace is not None else pool.workspace(p.T)
+    to, ip, wk = p.dev_ptrs()
+    _check(lib().lora_delta(pool.handle, x.data_ptr(), to, ip, wk, ctypes.byref(p.info), y.data_ptr(), ws.data_ptr(),
+                            ws.numel() * ws.element_size(), _stream(x.device)), "lora_delta")
+    return y
+
+
+def correction_bgmv(x: torch.Tensor, pool: Pool, slot_ids: torch.Tensor, y: torch.Tensor,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """lora_delta_bgmv: y += per-row adapter correction, token by token from
+    device slot ids (no plan)."""
+    tdt = _TORCH_DTYPE[pool.dtype]
+    _dev_tensor(slot_ids, torch.int32, "slot_ids")
+    T = int(slot_ids.shape[0])
+    _dev_tensor(x, tdt, "x", (T, pool.d_in))
+    _dev_tensor(y, tdt, "y", (T, pool.d_out))
+    ws = workspace if workspace is not None else pool.workspace(T)
+    _check(lib().lora_delta_bgmv(pool.handle, x.data_ptr(), slot_ids.data_ptr(), T, y.data_ptr(), ws.data_ptr(),
+                                 ws.numel() * ws.element_size(), _stream(x.device)), "lora_delta_bgmv")
+    return y
 
 
 def profile_begin(max_records: int = 100000):

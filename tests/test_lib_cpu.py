@@ -72,6 +72,38 @@ def test_plan_matches_oracle(seed):
     assert p.info.n_items <= lora.lib().lora_plan_max_items(T, S) or T == 0
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+@pytest.mark.parametrize("seed", range(12))
+def test_chunked_plan_matches_oracle(seed, chunk):
+    """lora_plan_chunked: the same token order and CSR offsets as lora_plan,
+    and the oracle's work list cut at `chunk` rows."""
+    g = np.random.default_rng(1000 + seed)
+    S = int(g.integers(1, 120))
+    T = int(g.integers(0, 5000))
+    ids = (np.minimum(g.zipf(1.1, size=T) - 1, S - 1) if seed % 2 else g.integers(0, S, size=T)).astype(np.int32)
+    p = lora.plan(ids, S, upload=False, chunk=chunk)
+    order, indptr, counts = oracle.plan(ids, S)
+    np.testing.assert_array_equal(p.token_order, order)
+    np.testing.assert_array_equal(p.slot_indptr, indptr)
+    wl = oracle.work_list(indptr, chunk)
+    np.testing.assert_array_equal(p.work[:, :3], wl)
+    assert p.info.chunk == chunk and p.info.n_items == len(wl)
+    assert p.info.n_items <= lora.lib().lora_plan_max_items(T, S) or T == 0
+
+
+def test_chunked_plan_errors():
+    L = lora.lib()
+    info = lora.PlanInfo()
+    ids = np.array([1, 2, 1], np.int32)
+    out = np.zeros(64, np.int32)
+    for bad in (0, 8, 24, 256):
+        assert L.lora_plan_chunked(3, ids.ctypes.data, 3, bad, out.ctypes.data, out[8:].ctypes.data,
+                                   out[16:].ctypes.data, 8, ctypes.byref(info)) == lora.LORA_EINVAL
+    assert L.lora_plan(3, ids.ctypes.data, 3, out.ctypes.data, out[8:].ctypes.data, out[16:].ctypes.data, 8,
+                       ctypes.byref(info)) == lora.LORA_OK
+    assert info.chunk == lora.LORA_PLAN_ROWS
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_plan_configs(cfg):
     from rank_gemm_amd.inputs import make_config
@@ -182,3 +214,10 @@ def test_device_plan_sizes_and_argument_errors():
 def test_bgmv_shrink_argument_errors():
     L = lora.lib()
     assert L.lora_shrink_bgmv(None, 1, 1, 4, 1, 1, 1 << 20, None) == lora.LORA_EINVAL
+
+
+def test_delta_argument_errors():
+    L = lora.lib()
+    info = lora.PlanInfo()
+    assert L.lora_delta(None, 1, 1, 1, 1, ctypes.byref(info), 1, 1, 1 << 20, None) == lora.LORA_EINVAL
+    assert L.lora_delta_bgmv(None, 1, 1, 4, 1, 1, 1 << 20, None) == lora.LORA_EINVAL
