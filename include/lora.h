@@ -341,6 +341,26 @@ int lora_delta_bgmv(const lora_pool* pool, const void* x, const int32_t* slot_id
                     size_t workspace_bytes, void* stream);
 
 /*
+ * lora_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are those of lora_linear, without the
+ * workspace: the kernels use a device array inside the library instead, of
+ * LORA_NOALLOC_MAX_WORKSPACE bytes, one per GPU, held from the first call on
+ * that GPU until the process ends. The call allocates and frees nothing. It
+ * runs on the current device (`stream` must belong to it). A call whose
+ * lora_workspace_bytes(pool, info->T) exceeds LORA_NOALLOC_MAX_WORKSPACE
+ * returns LORA_ESPACE and launches nothing. All calls on one GPU share that
+ * GPU's array: calls that may overlap on one GPU (two streams, two threads)
+ * race on it, so overlapping callers must use lora_linear with separate
+ * workspaces. The array keeps the last call's contents; no kernel depends on
+ * it starting at zero.
+ */
+#define LORA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+int lora_linear_noalloc(const lora_pool* pool, const void* x, const void* W, const int32_t* token_order,
+                        const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info, void* y,
+                        void* stream);
+
+/*
  * Per-kernel timing, for diagnostics and the benchmark's roofline figures.
  * Between lora_profile_begin and lora_profile_end, lora_linear,
  * lora_linear_multi and lora_shrink record a HIP event pair around every

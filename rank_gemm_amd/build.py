@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "plan.cpp", "pool.hip", "gemm_bf16.hip", "splitk.hip", "generic.hip", "sgmv.hip",
-           "plan_device.hip", "delta.hip"]
+           "plan_device.hip", "delta.hip", "noalloc.hip"]
 
 # Packed fp32 instructions are kept out of every kernel (-packed-fp32-ops).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -31,8 +31,10 @@ EXPORTS = (
     "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_workspace_bytes_multi",
     "lora_linear_multi", "lora_plan_device_words", "lora_plan_device", "lora_linear_device_plan",
     "lora_shrink_bgmv", "lora_linear_multi_device_plan", "lora_plan_chunked", "lora_delta", "lora_delta_bgmv",
+    "lora_linear_noalloc",
 )
 LORA_DEVICE_PLAN_MAX_SLOTS = 4096
+LORA_NOALLOC_MAX_WORKSPACE = 32 << 20
 LORA_MAX_SLICES = 4
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -84,6 +86,7 @@ def lib():
             L.lora_plan_chunked.argtypes = [_I, _P, _I, _I, _P, _P, _P, _I, ctypes.POINTER(PlanInfo)]
             L.lora_delta.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
             L.lora_delta_bgmv.argtypes = [_P, _P, _P, _I, _P, _P, _SZ, _P]
+            L.lora_linear_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P]
             L.lora_workspace_bytes.argtypes = [_P, _I]
             L.lora_workspace_bytes.restype = _SZ
             L.lora_linear.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PlanInfo), _P, _P, _SZ, _P]
