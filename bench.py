@@ -59,7 +59,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first: the clocks take a few tens of ms of this load to settle")
     ap.add_argument("--layers", type=int, default=32, help="layers of the decode-step figure")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--profile-steps", type=int, default=20)
@@ -197,7 +198,7 @@ def headline(args, torch, np, lora, acc, w3):
             "flops_per_launch": gemm_fl, "mean_us": round(t_gemm, 2),
             "median_us": round(us_of(stats, "gemm_bf16", "median_ms"), 2),
             "launches": stats.get("gemm_bf16", {}).get("count", 0)}
-    call_us = sum(v["mean_ms"] for v in stats.values()) * 1e3 / 2
+    call_us = t_shrink + t_gemm
     call_fl = base_fl + expand_fl + shrink_fl
     call = {"T_a": T_a, "active_slots": len(seg), "shrink_us": round(t_shrink, 2), "gemm_us": round(t_gemm, 2),
             "kernels_us_per_call": round(call_us, 2),
@@ -293,11 +294,12 @@ def decode_step(args, torch, np, lora, acc, make_config, make_qkv_decode):
     ms_step = el * 1e3 / args.decode_steps
 
     def profile(plan_ids):
+        # planned once: re-planning each step would make the host wait for the
+        # plan upload two steps back and let the GPU idle between layers
         lora.plan_into(p, plan_ids)
         f = filler(torch)
         lora.profile_begin(8 * L * args.profile_steps + 64)
         for _ in range(args.profile_steps):
-            lora.plan_into(p, plan_ids)
             layers_once()
         stats = lora.profile_end()
         torch.cuda.synchronize()

@@ -35,16 +35,19 @@ namespace lora {
 // direct-to-LDS loads (global_load_lds_dwordx4: 16 B per lane, written at the
 // instruction's LDS base + 16 * lane). A row of a stage is one 128-byte line
 // (8 chunks of 16 B). Rows go in groups of 64; load instruction q (0..7) of a
-// group fetches rows q, q + 8, ..., q + 56, lane l taking chunk l % 8 of row
-// q + 8 (l / 8): every 8 lanes read one whole line in order, which the memory
-// pipeline sends as one 128-byte request. The instruction's 1 KB lands at
-// q * 1040 bytes into the group, and that 16-byte pad per instruction puts
-// rows q = 0..7 on 8 different bank offsets, so the MFMA fragment reads (row
-// r0 + l % 16, chunk l / 16 of a 32-k half) are free of bank conflicts.
+// group fetches rows q, q + 8, ..., q + 56, the 8 lanes 8 i .. 8 i + 7 one
+// whole line of row q + 8 i, so the instruction's 1 KB lands at q * 1024 in
+// the group. Lane 8 i + j takes chunk j ^ q of its row (the XOR swizzle of
+// the chunk by the row's index within its 8-row stripe): the MFMA fragment
+// read of chunk c over 16 consecutive rows then finds their pieces at 16
+// distinct 16-byte slots of one aligned 256-byte window modulo 1 KB, which
+// this LDS serves in the minimum 4 cycles per ds_read_b128. (Rows merely
+// padded apart by 16 bytes spread those pieces over two windows for chunks
+// past the first: 8 cycles per read.)
 // Stage kt + NS - 1 is loaded once every wave is past stage kt's barrier. The
 // fragment reads are issued and waited on by hand: with LDS loads in flight
 // the compiler would wait for all of them at the first use.
-constexpr int kInstrBytes = 1040;              // 1 KB of 8 rows + 16 B pad
+constexpr int kInstrBytes = 1024;              // 1 KB of 8 rows
 constexpr int kGroupBytes = 8 * kInstrBytes;   // 64 rows
 
 // byte offset of the 16-row block starting at row r0 (r0 % 16 == 0)
@@ -128,13 +131,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     for (int b = 0; b < DA; ++b) {
         const int u = wave * DA + b;  // load instruction: group u / 8, rows u % 8 + 8 i
         prow[b] = m0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + cl * 8;
+        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + (cl ^ (u & 7)) * 8;
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
         const int u = wave * DB + b;
         ncol[b] = n0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + cl * 8;
+        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + (cl ^ (u & 7)) * 8;
     }
     __syncthreads();  // slot metadata staged
     // the same for every lane; read from LDS it would be a per-lane value, and
@@ -150,25 +153,36 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     auto issue = [&](int kt) {
         u32x4* st = lds + (kt % NS) * STAGE;
         gptr<u32x4> asrc[DA], bsrc[DB];
+        // the chunk lane cl fetches with load instruction u: cl ^ (u % 8)
         if (kt >= ne) {
             const int k = (kt - ne) * BK;
-            const bool kin = !KTAIL || k + cl * 8 < K;  // K % 8 == 0: a chunk is fully in or out
 #pragma unroll
-            for (int b = 0; b < DA; ++b) asrc[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
+            for (int b = 0; b < DA; ++b) {  // K % 8 == 0: a chunk is fully in or out
+                const bool kin = !KTAIL || k + (cl ^ ((wave * DA + b) & 7)) * 8 < K;
+                asrc[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
+            }
 #pragma unroll
-            for (int b = 0; b < DB; ++b) bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
+            for (int b = 0; b < DB; ++b) {
+                const bool kin = !KTAIL || k + (cl ^ ((wave * DB + b) & 7)) * 8 < K;
+                bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
+            }
         } else {
             const ExtraStep x = cur.current();
             cur.advance();
-            const int k = x.t * BK + cl * 8;        // position in the 2 rp extension
-            const int q = k < f.rp ? k : k - f.rp;  // rank of the chunk (rp % 8 == 0)
-            const bool qin = k < 2 * f.rp && q < x.r;
 #pragma unroll
-            for (int b = 0; b < DA; ++b)
+            for (int b = 0; b < DA; ++b) {
+                const int k = x.t * BK + (cl ^ ((wave * DA + b) & 7)) * 8;  // position in the 2 rp extension
+                const int q = k < f.rp ? k : k - f.rp;                      // rank of the chunk (rp % 8 == 0)
+                const bool qin = k < 2 * f.rp && q < x.r;
                 asrc[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
+            }
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+            for (int b = 0; b < DB; ++b) {
+                const int k = x.t * BK + (cl ^ ((wave * DB + b) & 7)) * 8;
+                const int q = k < f.rp ? k : k - f.rp;
+                const bool qin = k < 2 * f.rp && q < x.r;
                 bsrc[b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+            }
         }
 #pragma unroll
         for (int b = 0; b < DA; ++b) {
@@ -191,9 +205,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     uint32_t abase[2], bbase[2];  // per 32-k half of a stage
     const uint32_t lane_off = lds_offset(lds) + (fr & 7) * kInstrBytes + (fr >> 3) * 128;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        abase[h] = lane_off + block_off(wm * FI * 16) + (h * 4 + fc) * 16;
-        bbase[h] = lane_off + ABYTES + block_off(wn * FJ * 16) + (h * 4 + fc) * 16;
+    for (int h = 0; h < 2; ++h) {  // chunk h * 4 + fc of row fr sits at slot (h * 4 + fc) ^ (fr % 8)
+        abase[h] = lane_off + block_off(wm * FI * 16) + ((h * 4 + fc) ^ (fr & 7)) * 16;
+        bbase[h] = lane_off + ABYTES + block_off(wn * FJ * 16) + ((h * 4 + fc) ^ (fr & 7)) * 16;
     }
 
 #pragma unroll
@@ -335,13 +349,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int b = 0; b < DA; ++b) {
         const int u = wave * DA + b;
         prow[b] = m0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + kb + cl * 8;
+        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + kb + (cl ^ (u & 7)) * 8;
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
         const int u = wave * DB + b;
         ncol[b] = n0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + kb + cl * 8;
+        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + kb + (cl ^ (u & 7)) * 8;
     }
     __syncthreads();  // slot metadata staged
     // the expand's extra steps; in a split, split kz takes extra steps kz,
@@ -357,13 +371,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // sources of step kt's load instructions (A 0..DA-1, then B); set once
     // per step, in step order (the cursor advances on extra steps)
     gptr<u32x4> src[ND];
+    // lane cl fetches chunk cl ^ (u % 8) with load instruction u
     auto sources_base = [&](int kt) {
         const int k = (kt - ne) * BK;
-        const bool kin = !KTAIL || k + cl * 8 < Kr;
 #pragma unroll
-        for (int b = 0; b < DA; ++b) src[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
+        for (int b = 0; b < DA; ++b) {
+            const bool kin = !KTAIL || k + (cl ^ ((wave * DA + b) & 7)) * 8 < Kr;
+            src[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
+        }
 #pragma unroll
-        for (int b = 0; b < DB; ++b) src[DA + b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
+        for (int b = 0; b < DB; ++b) {
+            const bool kin = !KTAIL || k + (cl ^ ((wave * DB + b) & 7)) * 8 < Kr;
+            src[DA + b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
+        }
     };
     // W is the left operand (acc holds blocks of W x^T, a lane 4 consecutive
     // columns of one row) except in a split, whose partials take the split-K
@@ -376,15 +396,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const ExtraStep x = cur.current();
 #pragma unroll 1
         for (int e = 0; e < ks; ++e) cur.advance();  // past the other splits' steps
-        const int k = x.t * BK + cl * 8;
-        const int q = k < f.rp ? k : k - f.rp;
-        const bool qin = k < 2 * f.rp && q < x.r;
 #pragma unroll
-        for (int b = 0; b < DA; ++b)
+        for (int b = 0; b < DA; ++b) {
+            const int k = x.t * BK + (cl ^ ((wave * DA + b) & 7)) * 8;
+            const int q = k < f.rp ? k : k - f.rp;
+            const bool qin = k < 2 * f.rp && q < x.r;
             src[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
+        }
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+        for (int b = 0; b < DB; ++b) {
+            const int k = x.t * BK + (cl ^ ((wave * DB + b) & 7)) * 8;
+            const int q = k < f.rp ? k : k - f.rp;
+            const bool qin = k < 2 * f.rp && q < x.r;
             src[DA + b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+        }
     };
     auto load_piece = [&](int g, int buf) {
         const int u = g < DA ? wave * DA + g : wave * DB + (g - DA);
@@ -394,9 +419,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const uint32_t lane_off = lds_offset(lds) + (fr & 7) * kInstrBytes + (fr >> 3) * 128;
     uint32_t abase[2], bbase[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        abase[h] = lane_off + block_off(wm * FI * 16) + (h * 4 + fc) * 16;
-        bbase[h] = lane_off + ABYTES + block_off(wn * FJ * 16) + (h * 4 + fc) * 16;
+    for (int h = 0; h < 2; ++h) {  // chunk h * 4 + fc of row fr sits at slot (h * 4 + fc) ^ (fr % 8)
+        abase[h] = lane_off + block_off(wm * FI * 16) + ((h * 4 + fc) ^ (fr & 7)) * 16;
+        bbase[h] = lane_off + ABYTES + block_off(wn * FJ * 16) + ((h * 4 + fc) ^ (fr & 7)) * 16;
     }
     u32x4 A0[FI], B0[FJ], A1[FI], B1[FJ];
     f32x4 acc[FI][FJ];
