@@ -201,6 +201,9 @@ EDGE = [
     (4096, 40, 4096, 5, [0, 16, 3, 8, 0], 16, "bf16"),       # 256 x 256 tiles, K shorter than one step
     (96, 1032, 200, 5, [0, 32, 20, 0, 31], 32, "bf16"),      # split-K, two items per shrink tile
     (80, 2048, 130, 4, [0, 48, 40, 33], 48, "bf16"),         # split-K, one item per shrink tile, 16 idle columns
+    (5000, 512, 7000, 9, [0, 16, 16, 8, 16, 16, 16, 16, 4], 16, "bf16"),  # 256 x 256 tiles: ragged M, many segments
+    (8200, 256, 16392, 5, [0, 80, 17, 0, 64], 80, "bf16"),    # 256 x 256: ragged M and N, K of 4 steps, 3 extra steps per slot
+    (4100, 320, 16384, 3, [0, 16, 8], 16, "bf16"),            # 256 x 256: 17 x 64 tiles, K of 5 steps, few adapters
     (37, 13, 100, 5, [0, 3, 0, 7, 1], 8, "bf16"),             # d_in % 8 != 0: element-generic kernels
     (70, 4099, 130, 4, [0, 16, 5, 2], 16, "bf16"),            # long odd K, ragged everything
     (64, 1, 16, 3, [0, 2, 1], 2, "bf16"),                     # a single input column
@@ -219,12 +222,35 @@ def test_edge_shapes(case):
         ids = np.repeat(g.integers(0, S, size=16), 256).astype(np.int32)
     if case == 14:  # 40 sequences of 100 tokens: segments that cross tile rows
         ids = np.repeat(g.integers(0, S, size=40), 100).astype(np.int32)
+    if EDGE[case][:3] == (8200, 256, 16392):  # 41 sequences of 200 tokens, some on slot 0
+        ids = np.repeat(g.integers(0, S, size=41), 200).astype(np.int32)
     alphas = [2.0 * r for r in ranks]
     w = make_custom(200 + case, T, d_in, d_out, S, ranks, alphas, ids, dtype=dtype, r_max=r_max)
     proj = w.projections[0]
     y, _, _ = run_layer(w, proj)
     ref, base = oracle_pair(w, proj)
     check_close(to_f64(y), ref, dtype, f"edge {EDGE[case]}", base)
+
+
+def test_prefill_gemm_base_only_bit_exact():
+    """The 256 x 256 kernel with a base-only plan (no extra steps) and with
+    the adapters (extra steps): rows on slot 0 agree bit for bit, and the
+    base-only output matches the oracle's base."""
+    T, d_in, d_out, S = 4608, 512, 8192, 5
+    ids = np.repeat(np.random.default_rng(12).integers(0, S, size=18), 256).astype(np.int32)
+    w = make_custom(47, T, d_in, d_out, S, [0, 16, 8, 16, 16], [0, 32, 16, 32, 32], ids, r_max=16)
+    proj = w.projections[0]
+    lora.profile_begin()
+    y_mix, pool, _ = run_layer(w, proj)
+    y_base, _, _ = run_layer(w, proj, pool=pool, slot_ids=np.zeros_like(ids))
+    stats = lora.profile_end()
+    assert stats["gemm_bf16"]["count"] == 2
+    rows = torch.from_numpy(ids == 0).cuda()
+    assert rows.any()
+    assert torch.equal(y_mix[rows].view(torch.int16), y_base[rows].view(torch.int16))
+    ref, base = oracle_pair(w, proj)
+    check_close(to_f64(y_mix), ref, "bf16", "256 x 256 mixed", base)
+    check_close(to_f64(y_base), base, "bf16", "256 x 256 base only", base)
 
 
 def test_unaligned_width_slot0_and_h():
