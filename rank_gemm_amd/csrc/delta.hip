@@ -25,19 +25,21 @@
 namespace lora {
 
 // ---------------------------------------------------------------- SGMV shrink --
-// grid (n_items, hs), 256 threads: the workgroup takes its item's 16-row
-// blocks in turn; for each, its 4 waves split K range kz and add their partial
+// grid (n_items, hs), 64 WAVES threads: the workgroup takes its item's 16-row
+// blocks in turn; for each, its waves split K range kz and add their partial
 // sums in wave order through LDS (shrink_item), into plane kz:
 //   part[kz][p][q] = sum_{k in range} x[t_p, k] A_s[q, k],   q < r_s
 // A_s is read from memory once per item; the item's later blocks find it in
 // the caches.
-__global__ __launch_bounds__(256) void delta_shrink_kernel(const uint16_t* __restrict__ X,
-                                                           const uint16_t* __restrict__ A_pool,
-                                                           const int32_t* __restrict__ rank,
-                                                           const int32_t* __restrict__ token_order,
-                                                           const Item* __restrict__ work, float* __restrict__ part,
-                                                           int T, int hkc, int K, int r_max) {
-    __shared__ f32x4 red[4 * 4 * 64];
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void delta_shrink_kernel(const uint16_t* __restrict__ X,
+                                                                  const uint16_t* __restrict__ A_pool,
+                                                                  const int32_t* __restrict__ rank,
+                                                                  const int32_t* __restrict__ token_order,
+                                                                  const Item* __restrict__ work,
+                                                                  float* __restrict__ part, int T, int hkc, int K,
+                                                                  int r_max) {
+    __shared__ f32x4 red[WAVES * 4 * 64];
     const Item it = work[blockIdx.x];
     const int r = rank[it.slot];
     if (r == 0) return;
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(256) void delta_shrink_kernel(const uint16_t* __res
     const ShrinkOut out{part + (int64_t)kz * T * r_max, nullptr, 0, 0.f};
     for (int b0 = 0; b0 < it.count; b0 += 16) {
         const Item sub{it.slot, it.begin + b0, min(16, it.count - b0), 0};
-        shrink_item<4>(X, A_pool, r, token_order, sub, out, K, kbeg, kend, r_max, red);
+        shrink_item<WAVES>(X, A_pool, r, token_order, sub, out, K, kbeg, kend, r_max, red);
     }
 }
 
@@ -165,8 +167,12 @@ hipError_t delta_sgmv(const uint16_t* X, const uint16_t* A_pool, const uint16_t*
                       int hs, int hkc, float* part, uint16_t* Y, int T, int N, int K, int r_max, hipStream_t st,
                       StageTimer* tm) {
     if (n_items == 0) return hipSuccess;
-    hipError_t e = launch(tm, "delta_shrink", delta_shrink_kernel, dim3(n_items, hs), dim3(256), st, X, A_pool,
-                          rank, token_order, (const Item*)work, part, T, hkc, K, r_max);
+    // few workgroups: 16 waves per item over the K range, else 4
+    hipError_t e = n_items * hs >= 256
+                       ? launch(tm, "delta_shrink", delta_shrink_kernel<4>, dim3(n_items, hs), dim3(256), st, X,
+                                A_pool, rank, token_order, (const Item*)work, part, T, hkc, K, r_max)
+                       : launch(tm, "delta_shrink", delta_shrink_kernel<16>, dim3(n_items, hs), dim3(1024), st, X,
+                                A_pool, rank, token_order, (const Item*)work, part, T, hkc, K, r_max);
     if (e != hipSuccess) return e;
     return launch(tm, "delta_expand", delta_expand_kernel, dim3(n_items, (N + 63) / 64), dim3(256), st,
                   (const float*)part, hs, B_pool, rank, scale, token_order, (const Item*)work, Y, T, N, r_max);
