@@ -208,6 +208,9 @@ EDGE = [
     (70, 4099, 130, 4, [0, 16, 5, 2], 16, "bf16"),            # long odd K, ragged everything
     (64, 1, 16, 3, [0, 2, 1], 2, "bf16"),                     # a single input column
     (200, 7, 65, 4, [0, 4, 2, 3], 4, "f32"),                  # fp32, d_in below 8
+    (1100, 515, 1000, 6, [0, 16, 5, 0, 9, 12], 16, "bf16"),  # element-generic, 64 x 64 tiles (288 of them)
+    (1030, 256, 1030, 4, [0, 8, 3, 8], 8, "f32"),             # fp32, 64 x 64 tiles, ragged M and N
+    (64, 300, 2000, 5, [0, 8, 8, 8, 8], 8, "f32"),             # fp32, 32 x 32 tiles, many column tiles
 ]
 
 
