@@ -204,80 +204,126 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     tn = in / gsize;
 }
 
-// The expand as extra K steps of the tiled GEMM. For each slot s whose
-// segment meets the tile's rows [m0, mend) the K dimension is extended by
-// 2 rp (rp = r_max rounded up to 8): the A operand of row p is its ext row
-// [bf16 hi of scale_s h | lo remainder] (zero for rows of other segments),
-// the B operand of column n is [B_s[n] | B_s[n]], so the products add
-// scale_s h . B_s. The extension is walked in steps of 64 (or 32).
-struct ExtraStep {
-    int s, sb, se, r, t;
-};
-
-// Cursor over a tile's extra steps (slot, its segment, rank, step within the
-// slot), advanced once per extra step issued. The slot metadata is read from
-// its LDS copy (the host takes the extra-step form only for pools of at most
-// kMetaSlots slots): a flat or global load here would also wait for every
-// direct-to-LDS load in flight.
+// The expand as extra K steps of the tiled GEMM. The tile's live slots are
+// the slots s >= 1 of nonzero rank whose segment [indptr[s], indptr[s + 1])
+// is non-empty and meets the tile's rows [m0, mend); taken in slot order,
+// each extends K by 2 rp (rp = r_max rounded up to 8): the A operand of row
+// p is its ext row [bf16 hi of scale_s h | lo remainder] (zero for rows of
+// other segments), the B operand of column n is [B_s[n] | B_s[n]], so the
+// products add scale_s h . B_s. When 2 rp divides 64 (rp = 8, 16, 32) the
+// extensions of P = 64 / (2 rp) consecutive live slots share one 64-wide
+// step: every row belongs to one slot, so a row's products outside its own
+// slot's part are exact zeros. Otherwise each slot takes ceil(2 rp / 64)
+// steps of its own.
+//
+// The slot metadata is read from its LDS copy (the host takes the
+// extra-step form only for pools of at most kMetaSlots slots): a flat or
+// global load here would also wait for every direct-to-LDS load in flight.
 typedef const __attribute__((address_space(3))) SlotMeta* lds_meta_ptr;
-struct ExtraCursor {
-    lds_meta_ptr meta;
-    int S, m0, mend, spk;  // slots, the tile's rows [m0, mend), extra steps per slot
-    int cs, csb, cse, cr, ct;
-    __device__ __forceinline__ ExtraCursor(lds_meta_ptr m, int S_, int m0_, int mend_, int spk_)
-        : meta(m), S(S_), m0(m0_), mend(mend_), spk(spk_), cs(S_), csb(0), cse(0), cr(0), ct(0) {}
-    // first slot >= s whose segment meets the tile, with a nonzero rank
-    __device__ __forceinline__ void seek(int s) {
-        for (; s < S; ++s) {
-            const int sb = meta->indptr[s], se = meta->indptr[s + 1];
-            if (sb >= mend) {
-                s = S;
-                break;
-            }
-            const int r = meta->rank[s];
-            if (s != 0 && r != 0 && se > m0 && se > sb) {
-                csb = sb;
-                cse = se;
-                cr = r;
-                break;
-            }
-        }
-        cs = s;
-        ct = 0;
+
+typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr;  // slot ids (S <= kMetaSlots)
+
+// Live slots among slots 64 c .. 64 c + 63, as a wave-uniform bit mask.
+__device__ __forceinline__ uint64_t live_slots(lds_meta_ptr meta, int S, int m0, int mend, int c) {
+    const int s = 64 * c + (int)(threadIdx.x & 63);
+    bool live = false;
+    if (s >= 1 && s < S) {
+        const int sb = meta->indptr[s], se = meta->indptr[s + 1];
+        live = se > sb && sb < mend && se > m0 && meta->rank[s] != 0;
     }
-    // the tile's first extra step: from the last slot whose segment starts at or before m0
-    __device__ __forceinline__ void start() {
-        int lo = 0, hi = S - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (meta->indptr[mid] <= m0) lo = mid;
-            else hi = mid - 1;
-        }
-        seek(lo);
-    }
-    __device__ __forceinline__ ExtraStep current() const { return ExtraStep{cs, csb, cse, cr, ct}; }
-    __device__ __forceinline__ void advance() {
-        if (++ct == spk) seek(cs + 1);
-    }
+    return __ballot(live);
+}
+
+// The tile's extra steps: its live slots, listed in slot order in the
+// calling wave's own LDS list (no other wave reads it, so no barrier), and
+// how they map to steps.
+struct ExtraSched {
+    int n;    // live slots
+    int P;    // live slots per step (P > 1: 2 rp divides 64)
+    int spk;  // steps per slot (P == 1)
+    int lw;   // log2 of the 8-element chunks of one slot's part in a step
+    __device__ __forceinline__ int steps() const { return P > 1 ? (n + P - 1) / P : n * spk; }
 };
 
-// Number of extra steps of `step` k (e < 0) or the decoding of step e.
-__device__ __forceinline__ int extra_steps(const MetaView& mv, const Fuse& f, int m0, int mend, int e,
-                                           ExtraStep* out, int step = 64) {
-    int n = 0;
-    for (int s = slot_of(mv.indptr, f.S, m0); s < f.S; ++s) {
-        const int sb = mv.indptr[s], se = mv.indptr[s + 1];
-        if (sb >= mend) break;
-        const int r = mv.rank[s];
-        if (s == 0 || r == 0 || se <= m0 || se <= sb) continue;
-        const int k = (2 * f.rp + step - 1) / step;
-        if (e >= 0 && e < n + k) {
-            *out = ExtraStep{s, sb, se, r, e - n};
-            return e;
-        }
-        n += k;
+// on: the batch has adapter rows and the expand takes this form (the
+// metadata is staged in LDS); otherwise the tile has no extra step. `list`
+// holds at least min(S, mend - m0) entries (a live slot has a row in the tile).
+__device__ __forceinline__ ExtraSched extra_schedule(bool on, lds_meta_ptr meta, int S, int m0, int mend, int rp,
+                                                     lds_u16_ptr list) {
+    ExtraSched x;
+    const int r2 = on ? 2 * rp : 16;
+    x.P = (64 % r2 == 0) ? 64 / r2 : 1;
+    x.spk = x.P > 1 ? 1 : (r2 + 63) / 64;
+    x.lw = x.P == 4 ? 1 : x.P == 2 ? 2 : 3;
+    // chunks of 64 slots whose segments meet the tile: a chunk's segments
+    // span indptr[64 c] .. indptr[min(64 c + 64, S)]
+    int c_lo = 0, c_hi = on ? (S - 1) >> 6 : -1;
+    const int lane = (int)(threadIdx.x & 63);
+    if (c_hi > 0) {
+        bool meets = false;
+        if (lane <= c_hi) meets = meta->indptr[64 * lane] < mend && meta->indptr[min(64 * lane + 64, S)] > m0;
+        const uint64_t mm = __ballot(meets);
+        c_lo = mm ? __builtin_ctzll(mm) : 1;
+        c_hi = mm ? 63 - __builtin_clzll(mm) : 0;
     }
-    return n;
+    int n = 0;
+    for (int c = c_lo; c <= c_hi; ++c) {
+        const uint64_t mask = live_slots(meta, S, m0, mend, c);
+        if ((mask >> lane) & 1) list[n + __popcll(mask & ((1ull << lane) - 1))] = (uint16_t)(64 * c + lane);
+        n += __popcll(mask);
+    }
+    x.n = n;
+    return x;
+}
+
+// Operands of one load instruction's chunk in an extra step: chunk ch (0..7)
+// of the 64-wide step belongs to the step's slot e = ch >> lw; `k` is its
+// position in that slot's [hi | lo] part, `q` its rank, `ok` whether it
+// holds ranks below the slot's rank, [sb, se) the slot's segment.
+struct ExtraChunk {
+    int s, sb, se, k, q;
+    bool ok;
+};
+struct ExtraSlot {
+    int s, sb, se, r;
+};
+struct ExtraStepMeta {
+    ExtraSlot e0, e1, e2, e3;
+    int t;
+};
+// slot j of the list (none past the end: rank 0)
+__device__ __forceinline__ ExtraSlot extra_slot(lds_meta_ptr meta, lds_u16_ptr list, int n, int j) {
+    const bool has = j < n;
+    const int s = has ? list[has ? j : 0] : 0;
+    return ExtraSlot{s, meta->indptr[s], meta->indptr[s + 1], has ? meta->rank[s] : 0};
+}
+// extra step kt of the tile
+__device__ __forceinline__ ExtraStepMeta extra_step(const ExtraSched& x, lds_meta_ptr meta, lds_u16_ptr list,
+                                                    int kt) {
+    ExtraStepMeta m;
+    const int j0 = x.P > 1 ? kt * x.P : (x.spk == 1 ? kt : kt / x.spk);
+    m.t = x.P > 1 ? 0 : kt - j0 * x.spk;
+    const int n1 = x.P > 1 ? x.n : min(x.n, j0 + 1);  // P == 1: one slot per step
+    m.e0 = extra_slot(meta, list, n1, j0);
+    m.e1 = extra_slot(meta, list, n1, j0 + 1);
+    m.e2 = extra_slot(meta, list, x.P > 2 ? n1 : 0, j0 + 2);
+    m.e3 = extra_slot(meta, list, x.P > 2 ? n1 : 0, j0 + 3);
+    return m;
+}
+__device__ __forceinline__ ExtraChunk extra_chunk(const ExtraSched& x, const ExtraStepMeta& m, int ch, int rp) {
+    const int e = ch >> x.lw;
+    // field by field: a select between the structs themselves would take
+    // their addresses and put them in scratch memory
+    auto pick = [e](int v0, int v1, int v2, int v3) { return e == 0 ? v0 : e == 1 ? v1 : e == 2 ? v2 : v3; };
+    ExtraChunk c;
+    c.s = pick(m.e0.s, m.e1.s, m.e2.s, m.e3.s);
+    c.sb = pick(m.e0.sb, m.e1.sb, m.e2.sb, m.e3.sb);
+    c.se = pick(m.e0.se, m.e1.se, m.e2.se, m.e3.se);
+    const int r = pick(m.e0.r, m.e1.r, m.e2.r, m.e3.r);
+    c.k = m.t * 64 + ((ch & ((1 << x.lw) - 1)) << 3);
+    c.q = c.k < rp ? c.k : c.k - rp;
+    c.ok = c.k < 2 * rp && c.q < r;
+    return c;
 }
 
 // ------------------------------------------------- direct-to-LDS loads --

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     static_assert(FI <= 16 && NS >= 2 && (NS - 2) * DPW < 64, "wait counters");
     __shared__ u32x4 lds[NS * STAGE];
     __shared__ SlotMeta meta;
+    __shared__ uint16_t xlist[NW * BM];  // each wave's list of the tile's live slots
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const MetaView mv = stage_meta(f, &meta);
@@ -142,14 +143,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     __syncthreads();  // slot metadata staged
     // the same for every lane; read from LDS it would be a per-lane value, and
     // the loop would be compiled as divergent control flow
-    const int nt = __builtin_amdgcn_readfirstlane(
-        nk + ((f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0));
+    const lds_meta_ptr lmeta = (lds_meta_ptr)&meta;
+    const lds_u16_ptr wlist = (lds_u16_ptr)(xlist + wave * BM);
+    const ExtraSched xs = extra_schedule(f.adapters && f.ext, lmeta, f.S, m0, mend, f.rp, wlist);
+    const int nt = __builtin_amdgcn_readfirstlane(nk + xs.steps());
 
     // the expand's extra steps come first: their operands (B_s rows, scaled
     // h) are cold, and the base stages that follow hide their latency
     const int ne = nt - nk;
-    ExtraCursor cur((lds_meta_ptr)&meta, f.S, m0, mend, (2 * f.rp + BK - 1) / BK);
-    if (ne > 0) cur.start();
     auto issue = [&](int kt) {
         u32x4* st = lds + (kt % NS) * STAGE;
         gptr<u32x4> asrc[DA], bsrc[DB];
@@ -167,21 +168,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
                 bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
             }
         } else {
-            const ExtraStep x = cur.current();
-            cur.advance();
+            const ExtraStepMeta xm = extra_step(xs, lmeta, wlist, kt);
 #pragma unroll
             for (int b = 0; b < DA; ++b) {
-                const int k = x.t * BK + (cl ^ ((wave * DA + b) & 7)) * 8;  // position in the 2 rp extension
-                const int q = k < f.rp ? k : k - f.rp;                      // rank of the chunk (rp % 8 == 0)
-                const bool qin = k < 2 * f.rp && q < x.r;
-                asrc[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
+                const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DA + b) & 7), f.rp);
+                asrc[b] = or_zero(c.ok && prow[b] >= c.sb && prow[b] < c.se,
+                                  f.ext + (int64_t)prow[b] * 2 * f.rp + c.k);
             }
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
-                const int k = x.t * BK + (cl ^ ((wave * DB + b) & 7)) * 8;
-                const int q = k < f.rp ? k : k - f.rp;
-                const bool qin = k < 2 * f.rp && q < x.r;
-                bsrc[b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+                const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DB + b) & 7), f.rp);
+                bsrc[b] = or_zero(c.ok && ncol[b] < N, f.B_pool + ((int64_t)c.s * N + ncol[b]) * f.r_max + c.q);
             }
         }
 #pragma unroll
@@ -327,6 +324,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(NDA + NDB < 64 && NR <= 16, "wait counters");
     __shared__ u32x4 lds[NS * STAGE];
     __shared__ SlotMeta meta;
+    __shared__ uint16_t xlist[4 * BM];  // each wave's list of the tile's live slots
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const MetaView mv = stage_meta(f, &meta);
@@ -361,15 +359,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // the expand's extra steps; in a split, split kz takes extra steps kz,
     // kz + ks, kz + 2 ks, ... of the tile (the partials carry the correction)
     const int ks = SPLIT ? (int)gridDim.x / n_tiles : 1;
-    const int ne_all = (f.adapters && f.ext) ? extra_steps(mv, f, m0, mend, -1, nullptr, BK) : 0;
+    const lds_meta_ptr lmeta = (lds_meta_ptr)&meta;
+    const lds_u16_ptr wlist = (lds_u16_ptr)(xlist + wave * BM);
+    const ExtraSched xs = extra_schedule(f.adapters && f.ext, lmeta, f.S, m0, mend, f.rp, wlist);
+    const int ne_all = xs.steps();
     const int ne = __builtin_amdgcn_readfirstlane(SPLIT ? (ne_all > kz ? (ne_all - kz + ks - 1) / ks : 0) : ne_all);
     const int nt = nk + ne;
-    ExtraCursor cur((lds_meta_ptr)&meta, f.S, m0, mend, (2 * f.rp + BK - 1) / BK);
-    if (ne > 0) cur.start();
-    if constexpr (SPLIT)
-        for (int e = 0; e < kz && ne > 0; ++e) cur.advance();  // to this split's first extra step
-    // sources of step kt's load instructions (A 0..DA-1, then B); set once
-    // per step, in step order (the cursor advances on extra steps)
+    // sources of step kt's load instructions (A 0..DA-1, then B), set once
+    // per step
     gptr<u32x4> src[ND];
     // lane cl fetches chunk cl ^ (u % 8) with load instruction u
     auto sources_base = [&](int kt) {
@@ -392,23 +389,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if constexpr (SPLIT) mfma_agpr(c, a, w);
         else mfma_agpr(c, w, a);
     };
-    auto sources_extra = [&](int) {
-        const ExtraStep x = cur.current();
-#pragma unroll 1
-        for (int e = 0; e < ks; ++e) cur.advance();  // past the other splits' steps
+    auto sources_extra = [&](int kt) {
+        const ExtraStepMeta xm = extra_step(xs, lmeta, wlist, kz + ks * kt);  // the tile's step of this split
 #pragma unroll
         for (int b = 0; b < DA; ++b) {
-            const int k = x.t * BK + (cl ^ ((wave * DA + b) & 7)) * 8;
-            const int q = k < f.rp ? k : k - f.rp;
-            const bool qin = k < 2 * f.rp && q < x.r;
-            src[b] = or_zero(qin && prow[b] >= x.sb && prow[b] < x.se, f.ext + (int64_t)prow[b] * 2 * f.rp + k);
+            const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DA + b) & 7), f.rp);
+            src[b] = or_zero(c.ok && prow[b] >= c.sb && prow[b] < c.se, f.ext + (int64_t)prow[b] * 2 * f.rp + c.k);
         }
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-            const int k = x.t * BK + (cl ^ ((wave * DB + b) & 7)) * 8;
-            const int q = k < f.rp ? k : k - f.rp;
-            const bool qin = k < 2 * f.rp && q < x.r;
-            src[DA + b] = or_zero(qin && ncol[b] < N, f.B_pool + ((int64_t)x.s * N + ncol[b]) * f.r_max + q);
+            const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DB + b) & 7), f.rp);
+            src[DA + b] = or_zero(c.ok && ncol[b] < N, f.B_pool + ((int64_t)c.s * N + ncol[b]) * f.r_max + c.q);
         }
     };
     auto load_piece = [&](int g, int buf) {
@@ -709,8 +700,9 @@ static hipError_t tiled_shrink(const LinearArgs& L, const SliceArgs& sl, char* w
 }
 
 // One slice on the tiled path split over K: the shrink to the expand operand,
-// the 256 x 128 kernel writing partials (split 0 with the extra K steps), then
-// the split-K path's kernel 2 without adapters (adds the partials, rounds).
+// the 256 x 128 kernel writing partials (the extra K steps dealt round the
+// splits), then the split-K path's kernel 2 without adapters (adds the
+// partials, rounds).
 // Without the extra-step form of the expand (r_max % 8 != 0, or pools of more
 // than kMetaSlots slots), or when the extra steps would add more than a fifth
 // to a split, the slice runs unsplit.
@@ -719,11 +711,14 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
 static hipError_t split_tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
                                       StageTimer* tm) {
     const bool ext_ok = L.r_max % 8 == 0 && L.S <= kMetaSlots;
-    // extra steps per 256-row tile, bounded by the work items (16 rows of one
-    // slot each) that fall in 256 rows; spread over the splits they should
-    // stay small next to a split's base steps
+    // extra steps per 256-row tile, from the live slots of 256 rows bounded
+    // by the work items (16 rows of one slot each) that fall in them (64 /
+    // (2 rp) slots share a step when 2 rp divides 64); spread over the splits
+    // they should stay small next to a split's base steps
     const int64_t items_per_tile = ((int64_t)L.n_items * 256 + L.M - 1) / L.M;
-    const int64_t est_extra = (items_per_tile < L.S ? items_per_tile : (int64_t)L.S) * cdiv(2 * ((L.r_max + 7) & ~7), 64);
+    const int64_t slots_per_tile = items_per_tile < L.S ? items_per_tile : (int64_t)L.S;
+    const int r2 = 2 * ((L.r_max + 7) & ~7);
+    const int64_t est_extra = 64 % r2 == 0 ? (slots_per_tile * r2 + 63) / 64 : slots_per_tile * cdiv(r2, 64);
     if (L.adapters && (!ext_ok || est_extra * 5 > (int64_t)g.tks * (g.tkc / 64))) {
         GemmPlan gu = g;
         gu.tks = 0;

@@ -211,6 +211,9 @@ EDGE = [
     (1100, 515, 1000, 6, [0, 16, 5, 0, 9, 12], 16, "bf16"),  # element-generic, 64 x 64 tiles (288 of them)
     (1030, 256, 1030, 4, [0, 8, 3, 8], 8, "f32"),             # fp32, 64 x 64 tiles, ragged M and N
     (64, 300, 2000, 5, [0, 8, 8, 8, 8], 8, "f32"),             # fp32, 32 x 32 tiles, many column tiles
+    (3000, 264, 3000, 7, [0, 8, 5, 8, 3, 8, 1], 8, "bf16"),    # tiled, 4 slots share an extra step (2 rp = 16)
+    (2500, 520, 3000, 6, [0, 32, 17, 0, 30, 32], 32, "bf16"),  # tiled, one slot per extra step (2 rp = 64)
+    (2500, 264, 2600, 5, [0, 24, 9, 20, 24], 24, "bf16"),      # tiled, 2 rp = 48: one slot per step, partly empty
 ]
 
 
@@ -296,13 +299,16 @@ def test_block_starting_on_base_rows(r_max):
     check_close(to_f64(y), ref, w.dtype, f"block on base rows r_max={r_max}", base)
 
 
-@pytest.mark.parametrize("S,r_max,split", [(9, 16, True), (70, 8, False), (9, 5, False)])
+@pytest.mark.parametrize("S,r_max,split", [(9, 16, True), (70, 32, False), (70, 8, True), (9, 5, False), (9, 8, True),
+                                           (5, 32, True)])
 def test_tiled_split_over_k(S, r_max, split):
     """Mid-sized T with a long K runs the 256 x 128 tiled kernel split over K
     (fp32 partials, the expand's extra K steps dealt round the splits) and the
     split-K path's kernel 2 as the reduction; ragged d_out. The call runs
     unsplit when the expand needs its fp32 epilogue form (r_max % 8 != 0) or
-    when many short segments would make the extra steps a large share."""
+    when many short segments would make the extra steps a large share (70
+    slots at r_max 32: one slot per extra step; at r_max 8 four slots share
+    a step and the call splits)."""
     T, d_in, d_out = 512, 8192, 2100
     g = np.random.default_rng(S)
     ranks = np.minimum(g.integers(0, r_max + 1, size=S), r_max)
