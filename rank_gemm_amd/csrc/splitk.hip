@@ -327,7 +327,12 @@ __global__ __launch_bounds__(kThreads) void splitk_gemm_kernel(SplitArgs<MULTI ?
 // LDS (one more round). Dynamic LDS: 16 * r_max + 32 floats (the tail keeps
 // the last row's 32-rank reads in bounds; what they read there is not used).
 constexpr int kLaneMetaSlots = 64;
-constexpr int kMfmaSlots = 4;  // slots of a 16-row block whose expand kernel 2 runs on the matrix cores
+// distinct slots of a 16-row block whose expand kernel 2 runs on the matrix
+// cores: 4 for ranks up to 32 (one fragment per slot), 8 for ranks up to 64
+// (each of the 8 loads per slot pair costs a round-2 load in every block, so
+// the smaller count stays where it suffices)
+template <int MQ>
+constexpr int kMfmaSlots = MQ == 2 ? 8 : 4;
 
 template <bool ADAPT, bool VEC, bool LANE_META, bool MULTI, int MQ = 0>
 __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* __restrict__ part_y, int ks, int n_mt,
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
             sv = f.scale[min(lane, S - 1)];
         }
         // h: 16 rows x r_max, h_splits planes; 16-byte pieces when VEC
-        constexpr int HU = MQ == 1 ? 1 : 2;  // pieces per thread in round 1 (r_max <= 32: 16 r_max / 4 <= 256)
+        constexpr int HU = MQ > 0 ? 1 : 2;  // pieces per thread in round 1 (r_max <= 64: 16 r_max / 4 <= 256)
         const int rq = VEC ? r_max >> 2 : r_max;
         const int npc = 16 * rq;
         f32x4 hv[HU][8];
@@ -414,9 +419,12 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
             }
         }
         // slots of this lane's rows, of block row lane % 16 (row_slot) and of
-        // the block's first and last rows (its rows hold slots s_lo .. s_hi)
+        // the block's first and last rows (its rows hold slots s_lo .. s_hi);
+        // for MQ == 2 also smask, the set of non-zero slots of the block's
+        // rows (S <= 64)
         int sl[4] = {0, 0, 0, 0};
         int row_slot = 0, s_lo = 0, s_hi = 0;
+        uint64_t smask = 0;
         if constexpr (LANE_META) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -427,6 +435,7 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
                 if ((lane & 15) == j) row_slot = sj;
                 if (j == 0) s_lo = sj;
                 if (p0 + j < M) s_hi = sj;
+                if constexpr (MQ == 2) smask |= sj != 0 ? 1ull << sj : 0ull;
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -459,25 +468,52 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
 #pragma unroll
                 for (int c = 0; c < NC; ++c) b[e][c] = *or_zero(q0 + 8 * c < rr[e], bp[e] + q0 + 8 * c);
         };
-        // MQ > 0 (r_max <= 32 MQ) and at most kMfmaSlots slots in the block
+        // MQ > 0 (r_max <= 32 MQ) and at most NSL slots in the block
         // (uniform): the expand runs on the matrix cores, one pass per slot,
         // D[row][col] = sum_q (scale_s h[row][q]) B_s[col][q] over the rows
         // of slot s, the scaled h split into bf16 hi + lo (as the tiled
         // path's extra K steps). Round 2 then loads each slot's B fragments:
-        // lane l takes column l % 16 of the wave, ranks 32 c + 8 (l / 16) ..
+        // lane l takes column l % 16 of the wave, ranks 32 c + 8 (l / 16) ..,
+        // so a load instruction reads 64 consecutive bytes of each of 16
+        // columns. Slot k of the block: MQ == 1, s_lo + k up to s_hi (slot
+        // ids in between without rows included); MQ == 2, the k-th distinct
+        // slot (the k-th set bit of smask). S: none.
         constexpr int NQ = MQ > 0 ? MQ : 1;
-        const bool mx = MQ > 0 && s_hi - s_lo < kMfmaSlots;
-        u32x4 bf[kMfmaSlots][NQ];
+        constexpr int NSL = kMfmaSlots<MQ>;
+        const bool mx = MQ == 2 ? __popcll(smask) <= NSL : MQ > 0 && s_hi - s_lo < NSL;
+        auto distinct_slot = [&](int k) {  // MQ == 2: the k-th set bit of smask, S past the last
+            uint64_t m = smask;
+#pragma unroll
+            for (int i = 0; i < NSL; ++i)
+                if (i < k) m &= m - 1;
+            return m ? (int)__builtin_ctzll(m) : S;
+        };
+        u32x4 bf[NSL][NQ];
         if (mx) {
+            if constexpr (MQ == 2) {
 #pragma unroll
-            for (int k = 0; k < kMfmaSlots; ++k) {
-                const int sk = min(s_lo + k, S - 1);
-                const int rk_s = __shfl(rk, sk);
+                for (int k = 0; k < NSL; ++k) {
+                    const int s_k = distinct_slot(k);
+                    const int sk = min(s_k, S - 1);
+                    const int rk_s = __shfl(rk, sk);
 #pragma unroll
-                for (int c = 0; c < NQ; ++c) {
-                    const int q0 = 32 * c + 8 * (lane >> 4);
-                    const bool ok = s_lo + k <= s_hi && sk != 0 && q0 < rk_s && n < N;
-                    bf[k][c] = *or_zero(ok, f.B_pool + ((int64_t)sk * N + min(n, N - 1)) * r_max + q0);
+                    for (int c = 0; c < NQ; ++c) {
+                        const int q0 = 32 * c + 8 * (lane >> 4);
+                        const bool ok = s_k < S && q0 < rk_s && n < N;
+                        bf[k][c] = *or_zero(ok, f.B_pool + ((int64_t)sk * N + min(n, N - 1)) * r_max + q0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < NSL; ++k) {
+                    const int sk = min(s_lo + k, S - 1);
+                    const int rk_s = __shfl(rk, sk);
+#pragma unroll
+                    for (int c = 0; c < NQ; ++c) {
+                        const int q0 = 32 * c + 8 * (lane >> 4);
+                        const bool ok = s_lo + k <= s_hi && sk != 0 && q0 < rk_s && n < N;
+                        bf[k][c] = *or_zero(ok, f.B_pool + ((int64_t)sk * N + min(n, N - 1)) * r_max + q0);
+                    }
                 }
             }
         } else if constexpr (VEC) {
@@ -549,10 +585,8 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
             const int rk_row = __shfl(rk, row_slot);  // every lane takes part in the shuffle
             const int r_row = row_slot == 0 ? 0 : rk_row;
             f32x4 dm = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < kMfmaSlots; ++k) {
-                if (s_lo + k > s_hi) break;  // uniform
-                const bool mine = row_slot == s_lo + k && row_slot != 0;
+            // one slot's pass: rows of slot s (mine) times its B fragments
+            auto pass = [&](int k, bool mine) {
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
                     const int q0 = 32 * c + 8 * (lane >> 4);
@@ -573,6 +607,20 @@ __global__ __launch_bounds__(kThreads) void splitk_epilogue_kernel(const float* 
                                     pack_bf16x2(lo[6], lo[7])};
                     dm = mfma16x16x32(ahi, bf[k][c], dm);
                     dm = mfma16x16x32(alo, bf[k][c], dm);
+                }
+            };
+            if constexpr (MQ == 2) {
+#pragma unroll
+                for (int k = 0; k < NSL; ++k) {
+                    const int s_k = distinct_slot(k);
+                    if (s_k >= S) break;  // uniform
+                    pass(k, row_slot == s_k);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < NSL; ++k) {
+                    if (s_lo + k > s_hi) break;  // uniform
+                    pass(k, row_slot == s_lo + k && row_slot != 0);
                 }
             }
 #pragma unroll
@@ -643,10 +691,10 @@ static auto epilogue_for(const LinearArgs& L) {
     if (!L.adapters) return splitk_epilogue_kernel<false, false, false, MULTI>;
     if (L.r_max % 8 != 0) return splitk_epilogue_kernel<true, false, false, MULTI>;
     if (L.S <= kLaneMetaSlots) {
-        // the matrix-core expand for ranks up to 32 (at r_max 64 the per-lane
-        // B loads were measured faster: 12.1 against 13.0 us on a 33-slot
-        // batch of 256 rows)
+        // the matrix-core expand for ranks up to 64, the per-lane one past
+        // that (and for blocks of more distinct slots than kMfmaSlots<MQ>)
         if (L.r_max <= 32) return splitk_epilogue_kernel<true, true, true, MULTI, 1>;
+        if (L.r_max <= 64) return splitk_epilogue_kernel<true, true, true, MULTI, 2>;
         return splitk_epilogue_kernel<true, true, true, MULTI>;
     }
     return splitk_epilogue_kernel<true, true, false, MULTI>;
