@@ -7,9 +7,7 @@ from {0..16}; d_in 4096 -> d_out 14336; a 17-slot pool per projection
 (slots 1-16 rank 16, alpha 32; slot 0 the zero adapter). One step = the
 host plan (lora_plan) and its upload, then lora_linear for gate and for up
 over that one plan (each call: the SGMV shrink, then the base GEMM with the
-expand as extra K steps). Two plan buffers are used in turn, so a step's
-plan is copied on a side stream while the previous step's kernels run.
-Inputs, weights and pools are resident in HBM;
+expand as extra K steps). Inputs, weights and pools are resident in HBM;
 the step's working set (x 64 MiB, two W of 112 MiB, two y of 224 MiB) is
 three times the 256 MiB MALL, so every call streams from HBM.
 
@@ -169,28 +167,17 @@ def headline(args, torch, np, lora, acc, w3):
     Ws = [lora.to_device(pr.W, "bf16") for pr in projs]
     ys = [torch.empty((T, pr.d_out), dtype=torch.bfloat16, device="cuda") for pr in projs]
     ws = torch.empty(max(pl.workspace_bytes(T) for pl in pools), dtype=torch.uint8, device="cuda")
-    # Two device plans used in turn: step i's plan is computed on the host and
-    # copied on a side stream while step i - 1's kernels run; the copy waits
-    # for the kernels that last read its buffer (step i - 2), the step's
-    # kernels wait for the copy.
-    plans = [lora.plan(ids, S), lora.plan(ids, S)]
-    copy_stream = torch.cuda.Stream()
-    main = torch.cuda.current_stream()
-    read_done = [torch.cuda.Event(), torch.cuda.Event()]
-    turn = [0]
+    # The plan is computed on the host and copied on the compute stream ahead
+    # of the step's kernels. (Copying it on a side stream during the previous
+    # step saved about 10 us per step, but stalled single GEMM launches for
+    # several milliseconds now and then while both queues were busy.)
+    p = lora.plan(ids, S)
     torch.cuda.synchronize()
 
     def step():
-        k = turn[0]
-        turn[0] ^= 1
-        p = plans[k]
-        copy_stream.wait_event(read_done[k])
-        with torch.cuda.stream(copy_stream):
-            lora.plan_into(p, ids)
-        main.wait_stream(copy_stream)
+        lora.plan_into(p, ids)
         for W, pool, y in zip(Ws, pools, ys):
             lora.linear(x, W, pool, p, y=y, workspace=ws)
-        read_done[k].record(main)
 
     for _ in range(args.warmup):
         step()
@@ -273,7 +260,7 @@ def headline(args, torch, np, lora, acc, w3):
                 "note": "gate projection with a base-only plan (no correction kernel); torch.nn.functional.linear "
                         "(hipBLASLt) on the same x and W; stream events over 10 calls, best of 3 interleaved rounds"}
         log(f"headline base-only / library: {base}")
-    del pools, x, Ws, ys, ws, plans
+    del pools, x, Ws, ys, ws, p
     torch.cuda.empty_cache()
     return value, ms_per_step, roof, call, base, stats
 
@@ -648,8 +635,8 @@ def main():
                                f"plan + lora_linear(gate) + lora_linear(up) per step",
                    "T": w3.T, "d_in": pr.d_in, "d_out": pr.d_out, "S": w3.S, "rank": 16, "calls_per_step": 2,
                    "value_is": "tokens through one adapted linear per second = 2 T / step time",
-                   "mode": "eager calls; plan computed on the host and copied on a side stream during "
-                           "the previous step (two plans in turn); no per-kernel events in this pass"},
+                   "mode": "eager calls; plan computed on the host and copied ahead of the step's kernels; "
+                           "no per-kernel events in this pass"},
         "roofline": roof, "cpu_baseline": cpu,
         "call": call, "kernels": kstats(hstats), "base_only": base,
         "decode": dec, "other_configs": others, "cpu_oracle": cpu_table, "correction_crossover": crossover,

@@ -228,7 +228,9 @@ class Plan:
         self.host = host  # pinned int32: [work 4*n_work][token_order T][slot_indptr S+1]
         self.dev = dev
         self._n_work = n_work
-        self._stage, self._ev, self._turn = [None, None], [None, None], 0  # plan_into staging
+        # plan_into staging: two pinned buffers used in turn, the copy that
+        # last read each (None: not read yet), the one to write next
+        self._stage, self._ev, self._turn = [None, None], [None, None], 0
 
     def _off(self, which):
         if which == "work":
@@ -280,7 +282,16 @@ def plan(slot_ids, S: int, device="cuda", upload: bool = True, chunk: int = LORA
         _require_gpu()
         dev = torch.empty(total, dtype=torch.int32, device=device)
         dev.copy_(host, non_blocking=True)
-    return Plan(int(S), T, info, host, dev, n_work, int(chunk))
+    p = Plan(int(S), T, info, host, dev, n_work, int(chunk))
+    if upload:
+        # the staging buffers of plan_into, allocated now rather than on
+        # first use: pinning host memory stalls the kernels running then
+        ev = torch.cuda.Event()
+        ev.record()
+        p._stage = [host, torch.empty(total, dtype=torch.int32, pin_memory=True)]
+        p._ev = [ev, None]
+        p._turn = 1
+    return p
 
 
 def plan_into(p: Plan, slot_ids) -> Plan:
@@ -290,11 +301,11 @@ def plan_into(p: Plan, slot_ids) -> Plan:
     summary stay valid only while it is unchanged, which the caller checks.
 
     The plan is written into one of two pinned staging buffers that the plan
-    owns for its lifetime, in turn, and copied from there on the current
-    stream. Before a staging buffer is written again, the host waits for the
-    copy that last read it (two plans back). No pinned memory is allocated
-    per call: registering new host memory with the GPU stalls the kernels
-    running at that moment."""
+    owns for its lifetime (the first is the buffer lora_plan filled), in
+    turn, and copied from there on the current stream. Before a staging
+    buffer is written again, the host waits for the copy that last read it
+    (two plans back). No pinned memory is allocated here: registering new
+    host memory with the GPU stalls the kernels running at that moment."""
     ids = np.ascontiguousarray(np.asarray(slot_ids), dtype=np.int32)
     if ids.ndim != 1 or ids.shape[0] != p.T:
         raise ValueError("plan_into needs the same T and S")
@@ -302,8 +313,7 @@ def plan_into(p: Plan, slot_ids) -> Plan:
         raise ValueError("plan was not uploaded")
     k = p._turn
     p._turn ^= 1
-    if p._stage[k] is None:
-        p._stage[k] = torch.empty(p.host.numel(), dtype=torch.int32, pin_memory=True)
+    if p._ev[k] is None:
         p._ev[k] = torch.cuda.Event()
     else:
         p._ev[k].synchronize()
