@@ -59,8 +59,10 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=20,
+    ap.add_argument("--steps", type=int, default=200,
+                    help="timed steps (a step of the headline takes ~1.5 ms; many steps average out the "
+                         "box's slower spells of some tens of milliseconds)")
+    ap.add_argument("--warmup", type=int, default=40,
                     help="untimed steps first: the clocks take a few tens of ms of this load to settle")
     ap.add_argument("--layers", type=int, default=32, help="layers of the decode-step figure")
     ap.add_argument("--decode-steps", type=int, default=50)
