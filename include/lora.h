@@ -26,6 +26,9 @@
  *    mlinterviewnotes.com).
  *  - Element type is the pool's: LORA_BF16 (uint16 bf16 bit patterns,
  *    fp32 accumulation, y rounded to nearest even) or LORA_F32.
+ *  - A call over T = 0 tokens returns LORA_OK at once, after checking the
+ *    pool and plan arguments; its x, W, y and workspace pointers may then be
+ *    null.
  *  - Widths are free: T, d_in, d_out and S take any value in range, and
  *    ragged tails are masked (the page's kernels "mask odd widths": section
  *    "Many adapters, one base-model batch"). bf16 pools whose d_in is a

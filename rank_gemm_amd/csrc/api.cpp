@@ -342,7 +342,7 @@ int lora_linear_device_plan(const lora_pool* p, const void* x, const void* W, co
 
 int lora_linear_multi_device_plan(const lora_slice* slices, int n, const void* x, const int32_t* plan, int T,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-    int rc = check_slices(slices, n, x, true);
+    int rc = check_slices(slices, n, x, false);  // buffers: checked by lora_linear_multi when T > 0
     if (rc != LORA_OK) return rc;
     const lora_pool* p0 = slices[0].pool;
     if (!plan || T < 0 || p0->S > LORA_DEVICE_PLAN_MAX_SLOTS) return LORA_EINVAL;
@@ -362,13 +362,17 @@ size_t lora_workspace_bytes_multi(const lora_slice* slices, int n, int T) {
 int lora_linear_multi(const lora_slice* slices, int n, const void* x, const int32_t* token_order,
                       const int32_t* slot_indptr, const int32_t* work, const lora_plan_info* info,
                       void* workspace, size_t workspace_bytes, void* stream) {
-    int rc = check_slices(slices, n, x, true);
+    // the pools first; the buffers only when there are rows (an empty batch
+    // may pass null or coinciding pointers for its empty outputs)
+    int rc = check_slices(slices, n, x, false);
     if (rc != LORA_OK) return rc;
     const lora_pool* p0 = slices[0].pool;
     rc = check_plan(p0, token_order, slot_indptr, work, info);
     if (rc != LORA_OK) return rc;
     const int T = info->T;
     if (T == 0) return LORA_OK;
+    rc = check_slices(slices, n, x, true);
+    if (rc != LORA_OK) return rc;
     if (!x) return LORA_EINVAL;
     if (!vector_path(p0)) {
         // element-generic pools: the slices one after another on the same

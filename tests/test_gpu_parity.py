@@ -238,6 +238,30 @@ def test_edge_shapes(case):
     check_close(to_f64(y), ref, dtype, f"edge {EDGE[case]}", base)
 
 
+@pytest.mark.parametrize("dtype,d_in", [("bf16", 256), ("f32", 96)])
+def test_empty_batch(dtype, d_in):
+    """T = 0: the layer, the multi-slice layer, the shrinks and the
+    correction alone return at once and touch nothing."""
+    S, ranks = 4, [0, 8, 4, 8]
+    w = make_custom(90, 0, d_in, 96, S, ranks, [2.0 * r for r in ranks], np.zeros(0, np.int32), dtype=dtype, r_max=8)
+    proj = w.projections[0]
+    pool = build_pool(w, proj)
+    x = lora.to_device(proj.x, dtype)
+    W = lora.to_device(proj.W, dtype)
+    p = lora.plan(np.zeros(0, np.int32), S)
+    assert p.info.T == 0 and p.info.n_items == 0
+    y = lora.linear(x, W, pool, p)
+    assert tuple(y.shape) == (0, 96)
+    ys = lora.linear_multi(x, [W, W.clone()], [pool, pool], p)
+    assert all(tuple(t.shape) == (0, 96) for t in ys)
+    h = lora.shrink(x, pool, p)
+    assert h.shape[0] == 0
+    lora.correction(x, pool, lora.plan(np.zeros(0, np.int32), S, chunk=64), y)
+    if dtype == "bf16":
+        lora.correction_bgmv(x, pool, torch.zeros(0, dtype=torch.int32, device="cuda"), y)
+    torch.cuda.synchronize()
+
+
 def test_prefill_gemm_base_only_bit_exact():
     """The 256 x 256 kernel with a base-only plan (no extra steps) and with
     the adapters (extra steps): rows on slot 0 agree bit for bit, and the
