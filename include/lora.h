@@ -30,8 +30,8 @@
  *    pool and plan arguments; its x, W, y and workspace pointers may then be
  *    null.
  *  - Widths are free: T, d_in, d_out and S take any value in range, and
- *    ragged tails are masked (the page's kernels "mask odd widths": section
- *    "Many adapters, one base-model batch"). bf16 pools whose d_in is a
+ *    ragged tails are masked (the kernels of "43. Beyond text", section
+ *    "Many adapters, one base-model batch", mask them too). bf16 pools whose d_in is a
  *    multiple of 8 run the matrix-core kernels, whose rows are read in
  *    16-byte pieces; fp32 pools and bf16 pools of any other d_in run the
  *    element-generic kernels (scalar loads, fp32 FMA, the expand fused into
@@ -278,8 +278,8 @@ int lora_linear_multi(const lora_slice* slices, int n, const void* x, const int3
 /*
  * The shrink alone, for inspection: h dev fp32 [T][r_max] receives
  * h[t][q] = sum_k x[t,k] A_s[q,k] for q < r_s, and 0 for q >= r_s and for
- * rows on slot 0 or a rank-0 slot (the "[tokens, r]-shaped" intermediate of
- * the mlinterviewnotes page, opening section). It uses the same per-item
+ * rows on slot 0 or a rank-0 slot (the T x r intermediate of the rank
+ * bottleneck, mlinterviewnotes page, opening section). It uses the same per-item
  * shrink code as lora_linear over the whole K range (lora_linear may split K
  * and add the splits, so the two agree to fp32 rounding, not bit for bit).
  * Errors as lora_linear.

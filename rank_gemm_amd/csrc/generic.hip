@@ -2,10 +2,10 @@
 // reduced-precision splitting) and bf16 pools whose d_in is not a multiple of
 // 8, where rows of x, W and A_s do not start on 16-byte boundaries and the
 // vector kernels' 16-byte loads do not apply. Every load here is a scalar
-// load, so any width works and K tails are masked element by element (the
-// page's kernels "accumulate in FP32, mask odd widths": "43. Beyond text:
-// images, embeddings, reranking and many LoRAs", section "Many adapters, one
-// base-model batch").
+// load, so any width works and K tails are masked element by element, with
+// fp32 accumulation, as the kernels of "43. Beyond text: images, embeddings,
+// reranking and many LoRAs", section "Many adapters, one base-model batch",
+// also do.
 //
 // Two kernels:
 //  1. shrink_generic_kernel: per work item (<= 16 rows of one slot's

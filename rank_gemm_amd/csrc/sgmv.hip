@@ -9,7 +9,7 @@
 // one matrix-core tile. Each item gathers its rows of x through token_order
 // and multiplies them by its own slot's A:
 //   h[p][q] = sum_k x[t_p, k] * A_s[q, k]     (fp32, p = sorted position)
-// the "[tokens, r]-shaped" intermediate of the same page. The waves of a
+// the narrow T x r intermediate of the same page. The waves of a
 // workgroup split K and their partial sums are added in wave order through
 // LDS, so h is deterministic. Rank masking ("SGLang: chunked SGMV, and a
 // rank-aware kernel"): rows q >= r_s of A are never loaded and a rank-0

@@ -3,9 +3,9 @@
 //
 // An item is <= 16 rows of one slot's segment (sorted positions begin ..
 // begin + count); its rows of x are gathered through token_order and
-// multiplied by the slot's A ("[tokens, r]-shaped in the middle": the
-// opening section of "LoRA serving, embeddings, rerankers, pooling",
-// mlinterviewnotes.com):
+// multiplied by the slot's A, giving the narrow T x r intermediate of the
+// rank bottleneck (opening section of "LoRA serving, embeddings, rerankers,
+// pooling", mlinterviewnotes.com):
 //   out[p][q] = sum_{k in [kbeg, kend)} x[t_p, k] A_s[q, k],   q < r_s
 // Rows q >= r_s of A are never loaded (rank masking, "SGLang: chunked SGMV,
 // and a rank-aware kernel"). The WAVES waves split the K range; their

@@ -130,8 +130,8 @@ struct SplitArgs {
 //
 // A shrink tile of group g takes, as its row block i < G, the rows of work
 // item g G + i, and as its column c the rank q = c' % rc of item c' / rc's
-// slot (c' = 64 e + c), i.e. row q of that slot's A ("[tokens, r]-shaped in
-// the middle", opening section of "LoRA serving, embeddings, rerankers,
+// slot (c' = 64 e + c), i.e. row q of that slot's A (the T x r bottleneck
+// of the opening section of "LoRA serving, embeddings, rerankers,
 // pooling", mlinterviewnotes.com). Only the blocks pairing an item's rows
 // with its own slot's ranks are kept: they are h over the split's K range,
 // written to the split's h plane. Ranks at or past r_s are never loaded
