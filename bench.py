@@ -20,7 +20,7 @@ profiler on: each kernel launch carries a pair of HIP events on its own
 stream that the runtime stamps with the kernel's start and end
 (hipExtLaunchKernel). The value thus comes from launches without
 instrumentation, and the durations from the same steps run again. The dominant kernel is the tiled base GEMM
-(gemm_w4_kernel, matrix-core bound): achieved = its algorithmic FLOPs per
+(gemm_tile_kernel, matrix-core bound): achieved = its algorithmic FLOPs per
 launch (2 T d_in d_out for the base product plus 2 T_a r d_out for the
 expand it carries) / its mean duration over the second pass.
 
@@ -214,12 +214,12 @@ def headline(args, torch, np, lora, acc, w3):
     ach = gemm_fl / (t_gemm * 1e-6) / 1e12
     roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("gemm_w4_kernel<256, 256, 2, false, false, false>", "traffic_prefill_gate_up.json",
+            "traffic": measured_traffic("gemm_tile_kernel<256, 256, 2, 2, 2, false, false, false>", "traffic_prefill_gate_up.json",
                                         ("gemm_bf16.hip", "fuse.h", "common.h", "kernels.h")),
             "traffic_note": "bytes per launch between the L2s and the memory fabric (MALL/HBM): FETCH_SIZE x 2.0 + "
                             "WRITE_SIZE x 1.0 (a plain 256 MiB copy reads those factors), against 416 MB of "
                             "algorithmic bytes; each XCD fetches its own copy of its tiles' x and W blocks",
-            "kernel": "gemm_w4_kernel (tiled bf16 base GEMM, 256x256 tiles, expand as extra K steps)",
+            "kernel": "gemm_tile_kernel (tiled bf16 base GEMM, 256x256 tiles on 4 waves, expand as extra K steps)",
             "flops_per_launch": gemm_fl, "mean_us": round(t_gemm, 2),
             "median_us": round(us_of(stats, "gemm_bf16", "median_ms"), 2),
             "launches": stats.get("gemm_bf16", {}).get("count", 0),

@@ -234,9 +234,10 @@ __device__ __forceinline__ uint64_t live_slots(lds_meta_ptr meta, int S, int m0,
     return __ballot(live);
 }
 
-// The tile's extra steps: its live slots, listed in slot order in the
-// calling wave's own LDS list (no other wave reads it, so no barrier), and
-// how they map to steps.
+// The tile's extra steps: its live slots, listed in slot order in an LDS
+// list, and how they map to steps. Every wave computes the same schedule;
+// only the `writer` wave fills the list, so the workgroup passes a barrier
+// before any wave reads it (when n > 0, which is uniform over the workgroup).
 struct ExtraSched {
     int n;    // live slots
     int P;    // live slots per step (P > 1: 2 rp divides 64)
@@ -249,7 +250,7 @@ struct ExtraSched {
 // metadata is staged in LDS); otherwise the tile has no extra step. `list`
 // holds at least min(S, mend - m0) entries (a live slot has a row in the tile).
 __device__ __forceinline__ ExtraSched extra_schedule(bool on, lds_meta_ptr meta, int S, int m0, int mend, int rp,
-                                                     lds_u16_ptr list) {
+                                                     lds_u16_ptr list, bool writer) {
     ExtraSched x;
     const int r2 = on ? 2 * rp : 16;
     x.P = (64 % r2 == 0) ? 64 / r2 : 1;
@@ -269,7 +270,7 @@ __device__ __forceinline__ ExtraSched extra_schedule(bool on, lds_meta_ptr meta,
     int n = 0;
     for (int c = c_lo; c <= c_hi; ++c) {
         const uint64_t mask = live_slots(meta, S, m0, mend, c);
-        if ((mask >> lane) & 1) list[n + __popcll(mask & ((1ull << lane) - 1))] = (uint16_t)(64 * c + lane);
+        if (writer && ((mask >> lane) & 1)) list[n + __popcll(mask & ((1ull << lane) - 1))] = (uint16_t)(64 * c + lane);
         n += __popcll(mask);
     }
     x.n = n;
@@ -345,16 +346,6 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
     u32x4 r;
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
     return r;
-}
-// at most N LDS reads of this wave still outstanding; ties the wait to the
-// fragment registers so that no use of them moves above it
-template <int N>
-__device__ __forceinline__ void lds_landed(u32x4& a) {
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
-}
-template <int N>
-__device__ __forceinline__ void lds_landed(u32x4& a, u32x4& b) {
-    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
 }
 // at most N vector-memory ops of this wave outstanding, no LDS op
 template <int N>

@@ -16,9 +16,9 @@
 // Two paths, chosen by (T, d_out) only:
 //  * tiled (T above decode sizes, this file): one kernel template with K in
 //    stages of 64 through an LDS ring filled by direct-to-LDS loads; the
-//    macro tile is the largest of 256 x 256, 256 x 128, 128 x 128 (8 waves)
-//    and 64 x 128 (4 waves) that still gives most CUs a tile. The shrink runs
-//    before it as its own kernel.
+//    macro tile is the one of 256 x 256 (4 waves), 256 x 128, 128 x 128 and
+//    64 x 128 (8 waves) that takes the fewest rounds of 256 tiles times the
+//    tile's time. The shrink runs before it as its own kernel.
 //  * split-K (decode-sized T, splitk.hip): a K-split GEMM with the shrink in
 //    extra workgroups of the same launch, then a kernel that adds the splits
 //    and applies the expand.
@@ -44,209 +44,28 @@ namespace lora {
 // this LDS serves in the minimum 4 cycles per ds_read_b128. (Rows merely
 // padded apart by 16 bytes spread those pieces over two windows for chunks
 // past the first: 8 cycles per read.)
-// Stage kt + NS - 1 is loaded once every wave is past stage kt's barrier. The
-// fragment reads are issued and waited on by hand: with LDS loads in flight
-// the compiler would wait for all of them at the first use.
+// The fragment reads are issued and waited on by hand: with LDS loads in
+// flight the compiler would wait for all of them at the first use.
 constexpr int kInstrBytes = 1024;              // 1 KB of 8 rows
 constexpr int kGroupBytes = 8 * kInstrBytes;   // 64 rows
 
 // byte offset of the 16-row block starting at row r0 (r0 % 16 == 0)
 __host__ __device__ constexpr int block_off(int r0) { return (r0 / 64) * kGroupBytes + (r0 % 64) / 8 * 128; }
 
-// fragments I.. of N, 16-row blocks following the one at `base` (whose row
-// is a multiple of 16 * N, or of 64)
-template <int I, int N>
-__device__ __forceinline__ void read_frags(u32x4 (&fr)[N], uint32_t base) {
-    if constexpr (I < N) {
-        fr[I] = lds_read16<block_off(16 * I)>(base);
-        read_frags<I + 1, N>(fr, base);
-    }
-}
-template <int N, int I, int FJ>
-__device__ __forceinline__ void tie_frags(u32x4 (&fr)[FJ]) {
-    if constexpr (I < FJ) {
-        lds_landed<N>(fr[I]);
-        tie_frags<N, I + 1, FJ>(fr);
-    }
-}
-// MFMA rows I.. of the wave tile; row i waits for A fragment i only (the B
-// fragments and A fragment 0 were waited on before row 0). W is the left
-// operand: acc[i][j] is a block of (W x^T), a lane's 4 values are 4
-// consecutive output columns of one row.
-template <int I, int FI, int FJ>
-__device__ __forceinline__ void mfma_rows(f32x4 (&acc)[FI][FJ], u32x4 (&af)[FI], const u32x4 (&bf)[FJ]) {
-    if constexpr (I < FI) {
-        if constexpr (I > 0) lds_landed<FI - 1 - I>(af[I]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) acc[I][j] = mfma16x16x32(bf[j], af[I], acc[I][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_rows<I + 1, FI, FJ>(acc, af, bf);
-    }
-}
-// stage kt landed: at most `ahead` later stages (DPW loads each) in flight
-template <int A, int DPW>
-__device__ __forceinline__ void wait_stage(int ahead) {
-    if constexpr (A <= 0) {
-        vm_landed<0>();
-    } else {
-        if (ahead >= A) vm_landed<A * DPW>();
-        else wait_stage<A - 1, DPW>(ahead);
-    }
-}
-
-// EPI: the expand runs in the epilogue from fp32 h (r_max % 8 != 0);
-// otherwise it runs as extra K steps (or there is no adapter row).
-// KTAIL: K % BK != 0, the last base stage masks the chunks past K.
-template <int BM, int BN, int WM, int WN, int BK, int NS, bool EPI, bool KTAIL>
-__global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4))) void gemm_dma_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
-    int tiles_m, int tiles_n, Fuse f) {
-    constexpr int NW = WM * WN;
-    constexpr int FI = BM / WM / 16, FJ = BN / WN / 16;   // MFMA tiles of a wave
-    constexpr int DA = BM / 8 / NW, DB = BN / 8 / NW;     // load instructions of a wave per stage
-    constexpr int DPW = DA + DB;
-    constexpr int ABYTES = BM / 64 * kGroupBytes, STAGE = (BM + BN) / 64 * kGroupBytes / 16;  // 16-byte units
-    static_assert(BK == 64 && BM % 64 == 0 && BN % 64 == 0, "stage layout");
-    static_assert((FI & (FI - 1)) == 0 && (FJ & (FJ - 1)) == 0, "fragment blocks");
-    static_assert(DA * NW * 8 == BM && DB * NW * 8 == BN, "load instructions per wave");
-    static_assert(FI <= 16 && NS >= 2 && (NS - 2) * DPW < 64, "wait counters");
-    __shared__ u32x4 lds[NS * STAGE];
-    __shared__ SlotMeta meta;
-    __shared__ uint16_t xlist[NW * BM];  // each wave's list of the tile's live slots
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-    const MetaView mv = stage_meta(f, &meta);
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int mend = min(M, m0 + BM);
-    const int nk = (K + BK - 1) / BK;
-    // this lane's rows of the A and B pieces it loads (rows past M or N are
-    // clamped: their products land in outputs that are not stored)
-    const int rl = lane >> 3, cl = lane & 7;
-    int prow[DA], ncol[DB];
-    const uint16_t* ap[DA];
-    const uint16_t* bp[DB];
-#pragma unroll
-    for (int b = 0; b < DA; ++b) {
-        const int u = wave * DA + b;  // load instruction: group u / 8, rows u % 8 + 8 i
-        prow[b] = m0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        ap[b] = X + (int64_t)f.token_order[min(prow[b], M - 1)] * K + (cl ^ (u & 7)) * 8;
-    }
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-        const int u = wave * DB + b;
-        ncol[b] = n0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
-        bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + (cl ^ (u & 7)) * 8;
-    }
-    __syncthreads();  // slot metadata staged
-    // the same for every lane; read from LDS it would be a per-lane value, and
-    // the loop would be compiled as divergent control flow
-    const lds_meta_ptr lmeta = (lds_meta_ptr)&meta;
-    const lds_u16_ptr wlist = (lds_u16_ptr)(xlist + wave * BM);
-    const ExtraSched xs = extra_schedule(f.adapters && f.ext, lmeta, f.S, m0, mend, f.rp, wlist);
-    const int nt = __builtin_amdgcn_readfirstlane(nk + xs.steps());
-
-    // the expand's extra steps come first: their operands (B_s rows, scaled
-    // h) are cold, and the base stages that follow hide their latency
-    const int ne = nt - nk;
-    auto issue = [&](int kt) {
-        u32x4* st = lds + (kt % NS) * STAGE;
-        gptr<u32x4> asrc[DA], bsrc[DB];
-        // the chunk lane cl fetches with load instruction u: cl ^ (u % 8)
-        if (kt >= ne) {
-            const int k = (kt - ne) * BK;
-#pragma unroll
-            for (int b = 0; b < DA; ++b) {  // K % 8 == 0: a chunk is fully in or out
-                const bool kin = !KTAIL || k + (cl ^ ((wave * DA + b) & 7)) * 8 < K;
-                asrc[b] = KTAIL ? or_zero(kin, ap[b] + k) : as_global<u32x4>(ap[b] + k);
-            }
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const bool kin = !KTAIL || k + (cl ^ ((wave * DB + b) & 7)) * 8 < K;
-                bsrc[b] = KTAIL ? or_zero(kin, bp[b] + k) : as_global<u32x4>(bp[b] + k);
-            }
-        } else {
-            const ExtraStepMeta xm = extra_step(xs, lmeta, wlist, kt);
-#pragma unroll
-            for (int b = 0; b < DA; ++b) {
-                const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DA + b) & 7), f.rp);
-                asrc[b] = or_zero(c.ok && prow[b] >= c.sb && prow[b] < c.se,
-                                  f.ext + (int64_t)prow[b] * 2 * f.rp + c.k);
-            }
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DB + b) & 7), f.rp);
-                bsrc[b] = or_zero(c.ok && ncol[b] < N, f.B_pool + ((int64_t)c.s * N + ncol[b]) * f.r_max + c.q);
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < DA; ++b) {
-            const int u = wave * DA + b;
-            dma16(asrc[b], st + ((u >> 3) * kGroupBytes + (u & 7) * kInstrBytes) / 16);
-        }
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            const int u = wave * DB + b;
-            dma16(bsrc[b], st + (ABYTES + (u >> 3) * kGroupBytes + (u & 7) * kInstrBytes) / 16);
-        }
-    };
-
-    f32x4 acc[FI][FJ];
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int fr = lane & 15, fc = lane >> 4;
-    uint32_t abase[2], bbase[2];  // per 32-k half of a stage
-    const uint32_t lane_off = lds_offset(lds) + (fr & 7) * kInstrBytes + (fr >> 3) * 128;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {  // chunk h * 4 + fc of row fr sits at slot (h * 4 + fc) ^ (fr % 8)
-        abase[h] = lane_off + block_off(wm * FI * 16) + ((h * 4 + fc) ^ (fr & 7)) * 16;
-        bbase[h] = lane_off + ABYTES + block_off(wn * FJ * 16) + ((h * 4 + fc) ^ (fr & 7)) * 16;
-    }
-
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < nt) issue(s);
-    for (int kt = 0; kt < nt; ++kt) {
-        // stage kt landed for this wave (the ones issued after it may be in flight)
-        wait_stage<NS - 2, DPW>(nt - 1 - kt);
-        stage_barrier();
-        if (kt + NS - 1 < nt) issue(kt + NS - 1);  // into stage kt - 1's buffer
-        const uint32_t so = (kt % NS) * STAGE * 16;
-#pragma unroll
-        for (int h = 0; h < BK / 32; ++h) {
-            u32x4 bf[FJ], af[FI];
-            read_frags<0, FJ>(bf, bbase[h] + so);
-            read_frags<0, FI>(af, abase[h] + so);
-            tie_frags<FI - 1, 0, FJ>(bf);
-            lds_landed<FI - 1>(af[0]);
-            mfma_rows<0, FI, FJ>(acc, af, bf);
-        }
-    }
-    const int p0 = m0 + wm * FI * 16, nb = n0 + wn * FJ * 16;
-    if constexpr (EPI) fused_expand<FI, FJ>(acc, f, mv, p0, nb, M, N, lane);
-    // the stage buffers become the output staging area once every wave is past its last fragment read
-    static_assert(NW * FI * FJ * 16 * 16 * 2 <= NS * STAGE * 16, "output staging");
-    __syncthreads();
-    store_tile<FI, FJ>(acc, reinterpret_cast<char*>(lds) + wave * (FI * 16) * (FJ * 32), Y, f.token_order, p0, nb,
-                       M, N, lane);
-}
-
-// ------------------------------------------------ 256 x 256 on 4 waves --
-// One wave per SIMD, wave tile 128 x 128 (8 x 8 MFMA blocks, 256 fp32
-// accumulators), the same two-stage direct-to-LDS ring and row-group layout
-// as above. With the 128 x 128 wave tile a stage reads 2/3 of the LDS bytes
-// of the 8-wave 128 x 64 tiling, and the single wave on a SIMD keeps the
-// matrix core busy by interleaving everything else between its MFMAs:
-//   phase A of stage kt: 64 MFMAs on the first 32-k half (fragments F0),
-//     one fragment read of the second half (F1) every 4 MFMAs;
-//   the wave's loads of stage kt + 1 landed; barrier;
-//   phase B: 64 MFMAs on F1, one fragment read of stage kt + 1's first half
-//     and one 1 KB load of stage kt + 2 (into stage kt's buffer, which every
-//     wave has finished reading) every 4 MFMAs.
+// ------------------------------------------------- the pipelined tile --
+// Each wave owns a (BM / WM) x (BN / WN) block of 16 x 16 MFMA tiles (fp32
+// accumulators in AGPRs) and keeps its matrix core busy by interleaving all
+// other work between its MFMAs. A 64-wide step has two 32-wide halves:
+//   phase A of step kt: the MFMAs of the first half (fragments F0), one
+//     fragment read of the second half (F1) per group of MFMAs;
+//   the wave's loads of step kt + 1 landed; barrier;
+//   phase B: the MFMAs of F1, one fragment read of step kt + 1's first half
+//     per group, and the 1 KB loads of a later step.
+// 256 x 256 runs on 4 waves, one per SIMD, with 128 x 128 wave tiles: a step
+// reads 2/3 of the LDS bytes of an 8-wave 128 x 64 tiling. The smaller tiles
+// run on 8 waves, two per SIMD: with so few MFMAs per phase one wave per SIMD
+// hides too little of the fragment reads and barriers (a 4-wave 128 x 128
+// took 57.7 us against 47.3 us at T = 1024, 4096 -> 4096).
 // The accumulators are tied to AGPRs by issuing these MFMAs as inline asm
 // (left to itself the register allocator shuffles accumulators through
 // VGPRs at every loop back edge, ~400 copies per stage). The compiler then
@@ -257,29 +76,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
 __device__ __forceinline__ void mfma_agpr(f32x4& acc, const u32x4& a, const u32x4& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-template <int N>
-__device__ __forceinline__ void frags_landed(u32x4 (&a)[N]) {
-    static_assert(N == 4 || N == 8, "fragment count");
-    if constexpr (N == 8)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
-                     "+v"(a[6]), "+v"(a[7]));
-    else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
-}
-template <int NA, int NB>
-__device__ __forceinline__ void frags_retire(const u32x4 (&a)[NA], const u32x4 (&b)[NB]) {
-    static_assert((NA == 4 || NA == 8) && (NB == 4 || NB == 8), "fragment count");
-    if constexpr (NA == 8 && NB == 8)
-        asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
-                     "v"(a[6]), "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]),
-                     "v"(b[7]));
-    else if constexpr (NA == 8)
-        asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
-                     "v"(a[6]), "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
-    else
-        asm volatile("s_nop 7\n\ts_nop 7" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]),
-                     "v"(b[2]), "v"(b[3]));
-}
 template <int G>
 struct Idx {
     static constexpr int v = G;
@@ -287,6 +83,35 @@ struct Idx {
 template <class F, int... Gs>
 __device__ __forceinline__ void static_for(std::integer_sequence<int, Gs...>, F&& fn) {
     (fn(Idx<Gs>{}), ...);
+}
+template <int I, int N>
+__device__ __forceinline__ void frags_tie(u32x4 (&a)[N]) {
+    if constexpr (I < N) {
+        asm volatile("" : "+v"(a[I]));
+        frags_tie<I + 1, N>(a);
+    }
+}
+template <int I, int N>
+__device__ __forceinline__ void frags_use(const u32x4 (&a)[N]) {
+    if constexpr (I < N) {
+        asm volatile("" ::"v"(a[I]));
+        frags_use<I + 1, N>(a);
+    }
+}
+// every LDS read of this wave landed; ties the wait to the fragment
+// registers so that no use of them moves above it
+template <int N>
+__device__ __forceinline__ void frags_landed(u32x4 (&a)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]));
+    frags_tie<1, N>(a);
+}
+// 16 wait states during which the fragment registers stay live: the MFMAs
+// issued above may still read them
+template <int NA, int NB>
+__device__ __forceinline__ void frags_retire(const u32x4 (&a)[NA], const u32x4 (&b)[NB]) {
+    asm volatile("s_nop 7\n\ts_nop 7");
+    frags_use<0, NA>(a);
+    frags_use<0, NB>(b);
 }
 
 // Split over K (mid-sized T): block b takes tile b % n_tiles over the k
@@ -301,32 +126,32 @@ struct SplitOut {
     int n_mt, n_nt;  // 64 x 64 tile grid of the partials
 };
 
-// Tiles of BM x BN: 256 x 256 with 2 stages, 256 x 128 with 3 (150 KB). (A
-// 128 x 128 version on 4 waves, 64 x 64 wave tiles, took 57.7 us against
-// 47.3 us for the 8-wave kernel at T = 1024, 4096 -> 4096: with so few MFMAs
-// per phase one wave per SIMD hides too little.) Step kt + 2 is loaded during
-// step kt. With 3 stages its buffer was last read in step kt - 1, so its 1 KB
-// loads are spread over both phases of step kt; with 2 stages it is step kt's
-// own buffer, free only in phase B.
-template <int BM, int BN, int NS, bool EPI, bool KTAIL, bool SPLIT>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(
+// BM x BN tiles over WM x WN waves with NS stage buffers. With 2 stages, step
+// kt + 2 is loaded during step kt into step kt's own buffer, free only in
+// phase B. With NS >= 3, step kt + NS - 1 is loaded during step kt into the
+// buffer of step kt - 1 (every wave finished reading it before step kt - 1's
+// barrier), so its loads are spread over both phases.
+template <int BM, int BN, int WM, int WN, int NS, bool EPI, bool KTAIL, bool SPLIT>
+__global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, Fuse f, SplitOut so) {
     static_assert(!(SPLIT && EPI), "a split runs no expand");
-    constexpr int BK = 64;
-    constexpr int FI = BM / 32, FJ = BN / 32;              // MFMA blocks of a wave (BM / 2 x BN / 2)
-    constexpr int DA = BM / 32, DB = BN / 32, ND = DA + DB;  // load instructions of a wave per step
+    constexpr int BK = 64, NW = WM * WN;
+    constexpr int FI = BM / WM / 16, FJ = BN / WN / 16;    // MFMA blocks of a wave
+    constexpr int DA = BM / 8 / NW, DB = BN / 8 / NW, ND = DA + DB;  // load instructions of a wave per step
     constexpr int NM = FI * FJ, NR = FI + FJ;              // MFMAs and fragment reads per half step
     constexpr int ABYTES = BM / 64 * kGroupBytes, STAGE = (BM + BN) / 64 * kGroupBytes / 16;  // 16-byte units
-    static_assert((BM == 256 && BN == 256 && NS == 2) || (BM == 256 && BN == 128 && NS == 3), "tile configurations");
-    constexpr int NDA = NS >= 3 ? ND / 2 : 0;              // loads of step kt + 2 issued in phase A
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && DA * NW * 8 == BM && DB * NW * 8 == BN && NW % 4 == 0, "tile shape");
+    constexpr int L = NS >= 3 ? NS - 1 : 2;                // step kt + L is loaded during step kt
+    constexpr int NDA = NS >= 3 ? ND / 2 : 0;              // its loads issued in phase A
     constexpr int NDB = ND - NDA;                          // ... and in phase B
-    static_assert(NDA + NDB < 64 && NR <= 16, "wait counters");
+    constexpr int VM_MID = (L - 2) * ND + NDA;             // loads younger than step kt + 1's at mid-step
+    static_assert(NS >= 2 && VM_MID < 64 && (L - 1) * ND < 64 && NR <= 16, "wait counters");
     __shared__ u32x4 lds[NS * STAGE];
     __shared__ SlotMeta meta;
-    __shared__ uint16_t xlist[4 * BM];  // each wave's list of the tile's live slots
+    __shared__ uint16_t xlist[BM];  // the tile's live slots
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const MetaView mv = stage_meta(f, &meta);
     const int n_tiles = tiles_m * tiles_n;
     const int kz = SPLIT ? (int)blockIdx.x / n_tiles : 0;
@@ -360,8 +185,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // kz + ks, kz + 2 ks, ... of the tile (the partials carry the correction)
     const int ks = SPLIT ? (int)gridDim.x / n_tiles : 1;
     const lds_meta_ptr lmeta = (lds_meta_ptr)&meta;
-    const lds_u16_ptr wlist = (lds_u16_ptr)(xlist + wave * BM);
-    const ExtraSched xs = extra_schedule(f.adapters && f.ext, lmeta, f.S, m0, mend, f.rp, wlist);
+    const lds_u16_ptr wlist = (lds_u16_ptr)xlist;
+    const ExtraSched xs = extra_schedule(f.adapters && f.ext, lmeta, f.S, m0, mend, f.rp, wlist, wave == 0);
+    if (xs.n > 0) __syncthreads();  // the slot list written
     const int ne_all = xs.steps();
     const int ne = __builtin_amdgcn_readfirstlane(SPLIT ? (ne_all > kz ? (ne_all - kz + ks - 1) / ks : 0) : ne_all);
     const int nt = nk + ne;
@@ -421,15 +247,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // steps 0 and 1 in flight, step 0 landed, its first half read
+    // steps 0 .. L - 1 in flight, step 0 landed, its first half read
 #pragma unroll
-    for (int s0 = 0; s0 < 2; ++s0) {
+    for (int s0 = 0; s0 < L; ++s0) {
         if (s0 < ne) sources_extra(s0);
         else sources_base(min(s0, nt - 1));
 #pragma unroll
         for (int g = 0; g < ND; ++g) load_piece(g, s0);
     }
-    vm_landed<ND>();
+    vm_landed<(L - 1) * ND>();
     stage_barrier();
     static_for(std::make_integer_sequence<int, (FI > FJ ? FI : FJ)>{}, [&](auto ic) {
         constexpr int i = decltype(ic)::v;
@@ -442,12 +268,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if constexpr (r < FJ) B[r] = lds_read16<block_off(16 * r)>(bb);
         else A[r - FJ] = lds_read16<block_off(16 * (r - FJ))>(ab);
     };
-    // one step; `next` sets the sources of step kt + 2, loaded into buffer bn
+    // one step; `next` sets the sources of step kt + L, loaded into buffer bn
     // (step kt's own buffer with 2 stages: only after every wave has read it)
-    int bc = 0, bn = 2 % NS;  // buffers of step kt and of step kt + 2
+    int bc = 0, bn = L % NS;  // buffers of step kt and of step kt + L
     auto step = [&](int kt, auto&& next) {
         const uint32_t so = bc * STAGE * 16, sn = (bc + 1 == NS ? 0 : bc + 1) * STAGE * 16;
-        next(kt + 2);
+        next(kt + L);
         frags_landed(A0);
         frags_landed(B0);
         // phase A: MFMAs of the first half, reads of the second half
@@ -468,7 +294,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         frags_retire(A0, B0);
         frags_landed(A1);
         frags_landed(B1);
-        vm_landed<NDA>();  // step kt + 1 landed (this wave's loads; those of step kt + 2 issued above may not)
+        vm_landed<VM_MID>();  // step kt + 1 landed (this wave's loads; those of later steps may not)
         stage_barrier();
         // phase B: MFMAs of the second half, reads of step kt + 1's first half, the other loads
         static_for(std::make_integer_sequence<int, NR>{}, [&](auto gc) {
@@ -489,10 +315,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         bc = bc + 1 == NS ? 0 : bc + 1;
         bn = bn + 1 == NS ? 0 : bn + 1;
     };
-    // steps whose step kt + 2 is an extra step, then the rest (the last two
+    // steps whose step kt + L is an extra step, then the rest (the last L
     // steps reload the last step: the load count per step stays fixed)
     int kt = 0;
-    for (; kt + 2 < ne; ++kt) step(kt, sources_extra);
+    for (; kt + L < ne; ++kt) step(kt, sources_extra);
     for (; kt < nt; ++kt) step(kt, [&](int s) { sources_base(min(s, nt - 1)); });
     frags_landed(A0);
     frags_landed(B0);
@@ -516,7 +342,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         return;
     }
     if constexpr (EPI) fused_expand<FI, FJ>(acc, f, mv, p0, nb, M, N, lane);
-    static_assert(4 * FI * FJ * 16 * 16 * 2 <= NS * STAGE * 16, "output staging");
+    static_assert(NW * FI * FJ * 16 * 16 * 2 <= NS * STAGE * 16, "output staging");
     __syncthreads();
     store_tile<FI, FJ>(acc, reinterpret_cast<char*>(lds) + wave * (FI * 16) * (FJ * 32), Y, f.token_order, p0, nb, M,
                        N, lane);
@@ -528,14 +354,14 @@ GemmPlan gemm_bf16_plan(int M, int N, int K) {
     if (M <= 0 || N <= 0 || K <= 0) return g;  // nothing to launch
     // tiled path: the macro tile with the least (rounds of 256 tiles) x (time
     // of one tile); the relative tile times are measured ones (K = 4096:
-    // 256 x 256 96.5 us, 256 x 128 60 us, 128 x 128 47 us, 64 x 128 38 us)
+    // 256 x 256 96.5 us, 256 x 128 55 us, 128 x 128 39.5 us, 64 x 128 30 us)
     auto n_tiles = [&](int bm, int bn) { return (int64_t)cdiv(M, bm) * cdiv(N, bn); };
     if (n_tiles(256, 256) >= 200 || (M > 256 && n_tiles(64, 128) >= 128)) {
         struct Cand {
             int bm, bn;
             double t;
         };
-        constexpr Cand cands[] = {{256, 256, 96.5}, {256, 128, 60.0}, {128, 128, 47.0}, {64, 128, 38.0}};
+        constexpr Cand cands[] = {{256, 256, 96.5}, {256, 128, 55.0}, {128, 128, 39.5}, {64, 128, 30.0}};
         double best = 0.0;
         for (const Cand& c : cands) {
             const double cost = (double)((n_tiles(c.bm, c.bn) + 255) / 256) * c.t;
@@ -548,9 +374,9 @@ GemmPlan gemm_bf16_plan(int M, int N, int K) {
         // or 256 x 128 tiles split over K (few tiles, long K): each split's
         // tile time scales with its k range, plus its fp32 partial writes (at
         // 5 TB/s) and ~7 us of fill and drain; then the reduction reads the
-        // partials and writes y (at 4.4 TB/s, + 1 us). Measured: T = 512,
-        // 4096 -> 4096 28.5 + 8.1 us (no gain over 38 us unsplit);
-        // 14336 -> 4096 78 + 8 us against 122 us.
+        // partials and writes y (at 4.4 TB/s, + 1 us). Measured at T = 512:
+        // 14336 -> 4096 split 4 ways 63 + 7 us against ~105 us unsplit;
+        // 4096 -> 4096 stays unsplit (33 us).
         const double plain = best * K / 4096.0;
         double best_split = 0.9 * plain;  // taken only when clearly cheaper
         for (int ks = 2; ks <= 8; ks *= 2) {
@@ -558,7 +384,7 @@ GemmPlan gemm_bf16_plan(int M, int N, int K) {
             const int kse = cdiv(K, kc);
             if (kc < 512 || kse < 2) break;
             const double part_bytes = kse * (double)M * N * 4.0;
-            const double cost = (double)((n_tiles(256, 128) * kse + 255) / 256) * 60.0 * kc / 4096.0 +
+            const double cost = (double)((n_tiles(256, 128) * kse + 255) / 256) * 55.0 * kc / 4096.0 +
                                 part_bytes / 5.0e6 + 7.0 + (part_bytes + (double)M * N * 2.0) / 4.4e6 + 1.0;
             if (cost < best_split) {
                 best_split = cost;
@@ -646,36 +472,27 @@ size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max) 
     return need;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS>
-static hipError_t launch_dma(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
-                             bool epi, hipStream_t st, StageTimer* tm) {
-    const int tiles_m = cdiv(M, BM), tiles_n = cdiv(N, BN);
-    const bool ktail = K % BK != 0;
-    auto ker = epi ? (ktail ? gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, true>
-                            : gemm_dma_kernel<BM, BN, WM, WN, BK, NS, true, false>)
-                   : (ktail ? gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, true>
-                            : gemm_dma_kernel<BM, BN, WM, WN, BK, NS, false, false>);
-    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(64 * WM * WN), st, X, W, Y, M, N, K, tiles_m,
-                  tiles_n, f);
-}
-
-template <int BM, int BN, int NS, bool SPLIT_OK>
-static hipError_t launch_w4(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
+template <int BM, int BN, int WM, int WN, int NS, bool SPLIT_OK>
+static hipError_t launch_tile(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
                             bool epi, hipStream_t st, StageTimer* tm, const SplitOut& so = SplitOut{}, int ks = 1) {
     const int tiles_m = cdiv(M, BM), tiles_n = cdiv(N, BN);
     const bool ktail = K % 64 != 0;
-    decltype(&gemm_w4_kernel<BM, BN, NS, false, false, false>) ker;
+    const dim3 block(64 * WM * WN);
+    decltype(&gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, false>) ker;
     if constexpr (SPLIT_OK) {
         if (so.part) {
-            ker = ktail ? gemm_w4_kernel<BM, BN, NS, false, true, true> : gemm_w4_kernel<BM, BN, NS, false, false, true>;
-            return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n * ks), dim3(256), st, X, W, Y, M, N, K,
-                          tiles_m, tiles_n, f, so);
+            ker = ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, false, true, true>
+                        : gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, true>;
+            return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n * ks), block, st, X, W, Y, M, N, K, tiles_m,
+                          tiles_n, f, so);
         }
     }
-    ker = epi ? (ktail ? gemm_w4_kernel<BM, BN, NS, true, true, false> : gemm_w4_kernel<BM, BN, NS, true, false, false>)
-              : (ktail ? gemm_w4_kernel<BM, BN, NS, false, true, false> : gemm_w4_kernel<BM, BN, NS, false, false, false>);
-    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), dim3(256), st, X, W, Y, M, N, K, tiles_m, tiles_n,
-                  f, SplitOut{});
+    ker = epi ? (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, true, true, false>
+                       : gemm_tile_kernel<BM, BN, WM, WN, NS, true, false, false>)
+              : (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, false, true, false>
+                       : gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, false>);
+    return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), block, st, X, W, Y, M, N, K, tiles_m, tiles_n, f,
+                  SplitOut{});
 }
 
 // The shrink of the tiled path, into fp32 h [M][r_max] or, with ext, the
@@ -737,7 +554,7 @@ static hipError_t split_tiled_forward(const LinearArgs& L, const SliceArgs& sl, 
     const Fuse f{L.token_order, L.slot_indptr, nullptr, sl.B_pool, sl.rank, sl.scale, L.S, L.r_max, 1, 0, L.adapters,
                  ext, (L.r_max + 7) & ~7};
     const hipError_t e =
-        launch_w4<256, 128, 3, true>(L.X, sl.W, nullptr, M, N, K, f, false, st, tm, SplitOut{part, g.tkc, n_mt, n_nt},
+        launch_tile<256, 128, 4, 2, 3, true>(L.X, sl.W, nullptr, M, N, K, f, false, st, tm, SplitOut{part, g.tkc, n_mt, n_nt},
                                      g.tks);
     if (e != hipSuccess) return e;
     LinearArgs base = L;
@@ -765,10 +582,10 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
         if (e != hipSuccess) return e;
     }
     const bool epi = L.adapters && !f.ext;
-    if (g.bm == 256 && g.bn == 256) return launch_w4<256, 256, 2, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
-    if (g.bm == 256) return launch_w4<256, 128, 3, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
-    if (g.bm == 128) return launch_dma<128, 128, 2, 4, 64, 3>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
-    return launch_dma<64, 128, 2, 2, 64, 4>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256 && g.bn == 256) return launch_tile<256, 256, 2, 2, 2, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256) return launch_tile<256, 128, 4, 2, 3, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 128) return launch_tile<128, 128, 2, 4, 3, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    return launch_tile<64, 128, 2, 4, 4, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
 }
 
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {

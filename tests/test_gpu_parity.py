@@ -196,7 +196,7 @@ EDGE = [
     (400, 2056, 4000, 5, [0, 80, 17, 0, 64], 80, "bf16"),    # few items: K-split shrink, 2 rank groups
     (400, 2048, 4000, 4, [0, 3, 5, 2], 5, "bf16"),          # few items: K-split shrink to fp32 h
     (50, 512, 300, 4, [0, 256, 130, 1], 256, "bf16"),        # split-K, ranks past 64 (several B rounds)
-    (700, 264, 4096, 4, [0, 256, 130, 17], 256, "bf16"),     # 64 x 128 tiles, 8 extension steps per slot
+    (700, 264, 4096, 4, [0, 256, 130, 17], 256, "bf16"),     # 128 x 128 tiles, 8 extension steps per slot
     (4096, 64, 4096, 4, [0, 16, 8, 4], 16, "bf16"),          # 256 x 256 tiles, a single K step
     (4096, 40, 4096, 5, [0, 16, 3, 8, 0], 16, "bf16"),       # 256 x 256 tiles, K shorter than one step
     (96, 1032, 200, 5, [0, 32, 20, 0, 31], 32, "bf16"),      # split-K, two items per shrink tile
@@ -214,6 +214,10 @@ EDGE = [
     (3000, 264, 3000, 7, [0, 8, 5, 8, 3, 8, 1], 8, "bf16"),    # tiled, 4 slots share an extra step (2 rp = 16)
     (2500, 520, 3000, 6, [0, 32, 17, 0, 30, 32], 32, "bf16"),  # tiled, one slot per extra step (2 rp = 64)
     (2500, 264, 2600, 5, [0, 24, 9, 20, 24], 24, "bf16"),      # tiled, 2 rp = 48: one slot per step, partly empty
+    (1000, 264, 4000, 4, [0, 3, 5, 2], 5, "bf16"),             # 128 x 128 tiles (8 waves), epilogue expand
+    (1000, 40, 4000, 4, [0, 16, 3, 8], 16, "bf16"),            # 128 x 128 tiles, K shorter than one step
+    (500, 40, 4000, 5, [0, 80, 17, 0, 64], 80, "bf16"),        # 64 x 128 tiles, one K step, 3 extra steps per slot
+    (1800, 1000, 4000, 5, [0, 16, 8, 16, 4], 16, "bf16"),      # 256 x 128 tiles (8 waves), K tail
 ]
 
 
