@@ -327,17 +327,18 @@ def test_block_starting_on_base_rows(r_max):
     check_close(to_f64(y), ref, w.dtype, f"block on base rows r_max={r_max}", base)
 
 
-@pytest.mark.parametrize("S,r_max,split", [(9, 16, True), (70, 32, False), (70, 8, True), (9, 5, False), (9, 8, True),
-                                           (5, 32, True)])
-def test_tiled_split_over_k(S, r_max, split):
+@pytest.mark.parametrize("S,r_max,split,d_in", [(9, 16, True, 8192), (70, 32, False, 8192), (70, 8, True, 8192),
+                                                (9, 5, False, 8192), (9, 8, True, 8192), (5, 32, True, 8192),
+                                                (9, 16, True, 8200)])
+def test_tiled_split_over_k(S, r_max, split, d_in):
     """Mid-sized T with a long K runs the 256 x 128 tiled kernel split over K
     (fp32 partials, the expand's extra K steps dealt round the splits) and the
     split-K path's kernel 2 as the reduction; ragged d_out. The call runs
     unsplit when the expand needs its fp32 epilogue form (r_max % 8 != 0) or
     when many short segments would make the extra steps a large share (70
     slots at r_max 32: one slot per extra step; at r_max 8 four slots share
-    a step and the call splits)."""
-    T, d_in, d_out = 512, 8192, 2100
+    a step and the call splits). K = 8200 leaves the last split a K tail."""
+    T, d_out = 512, 2100
     g = np.random.default_rng(S)
     ranks = np.minimum(g.integers(0, r_max + 1, size=S), r_max)
     ranks[0] = 0
