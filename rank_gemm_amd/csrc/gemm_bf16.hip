@@ -23,6 +23,7 @@
 //    extra workgroups of the same launch, then a kernel that adds the splits
 //    and applies the expand.
 #include "fuse.h"
+#include "shrink.h"
 
 #include <type_traits>
 #include <utility>
@@ -428,6 +429,11 @@ static size_t tiled_workspace(int M, int r_max) {
     return ((h_final + 255) & ~size_t(255)) + planes;
 }
 
+// one slice's expand operand (bf16 hi / lo, [M][2][rp]) in the workspace
+static size_t ext_stride(int M, int r_max) {
+    return ((size_t)M * ((r_max + 7) & ~7) * sizeof(float) + 255) & ~size_t(255);
+}
+
 static int total_tiles_n(const int* N, int n_slices) {
     int t = 0;
     for (int i = 0; i < n_slices; ++i) t += cdiv(N[i], 64);
@@ -460,7 +466,8 @@ size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max) 
         g.n_nt = total_tiles_n(N, n_slices);
         return split_workspace(M, g.n_nt, g, n_slices, r_max);
     }
-    size_t need = 0;
+    // several slices may share one shrink: an expand operand area per slice
+    size_t need = n_slices > 1 ? n_slices * ext_stride(M, r_max) : 0;
     for (int i = 0; i < n_slices; ++i) {
         if (N[i] <= 0) continue;
         const GemmPlan g = gemm_bf16_plan(M, N[i], K);
@@ -524,7 +531,7 @@ static hipError_t tiled_shrink(const LinearArgs& L, const SliceArgs& sl, char* w
 // than kMetaSlots slots), or when the extra steps would add more than a fifth
 // to a split, the slice runs unsplit.
 static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
-                                StageTimer* tm);
+                                StageTimer* tm, uint16_t* ext_ready = nullptr);
 static hipError_t split_tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
                                       StageTimer* tm) {
     const bool ext_ok = L.r_max % 8 == 0 && L.S <= kMetaSlots;
@@ -564,9 +571,10 @@ static hipError_t split_tiled_forward(const LinearArgs& L, const SliceArgs& sl, 
 
 // One slice on the tiled path: the shrink to final h, then the tiled GEMM
 // with the expand fused (r_max % 8 == 0: as extra K steps from scaled h as
-// bf16 hi / lo; otherwise in the epilogue from fp32 h).
+// bf16 hi / lo; otherwise in the epilogue from fp32 h). With ext_ready the
+// expand operand was already written there (several slices, one shrink).
 static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const GemmPlan& g, hipStream_t st,
-                                StageTimer* tm) {
+                                StageTimer* tm, uint16_t* ext_ready) {
     if (g.tks > 1) return split_tiled_forward(L, sl, g, st, tm);
     const int M = L.M, N = sl.N, K = L.K;
     Fuse f{L.token_order, L.slot_indptr, nullptr, sl.B_pool, sl.rank, sl.scale, L.S, L.r_max, 1, 0, L.adapters,
@@ -575,9 +583,10 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
     float* hbuf = reinterpret_cast<float*>(ws);
     // the expand as extra K steps needs r_max % 8 == 0 and the slot metadata in LDS
     uint16_t* ext = (L.r_max % 8 == 0 && L.S <= kMetaSlots) ? reinterpret_cast<uint16_t*>(ws) : nullptr;
+    if (ext_ready) ext = ext_ready;
     f.h = ext ? nullptr : hbuf;
     f.ext = ext;
-    if (L.adapters) {
+    if (L.adapters && !ext_ready) {
         const hipError_t e = tiled_shrink(L, sl, ws, ext ? nullptr : hbuf, ext, st, tm);
         if (e != hipSuccess) return e;
     }
@@ -588,6 +597,22 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
     return launch_tile<64, 128, 2, 4, 4, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
 }
 
+// Several slices that all take the unsplit tiled path with the expand as
+// extra K steps share one shrink (x rows read once), each slice's operand in
+// its own workspace area; enough items that the single-slice shrink would not
+// split K either, so each operand equals that slice's own bit for bit.
+static bool slices_share_shrink(const LinearArgs& L, const int* N, GemmPlan* gs) {
+    if (L.n_slices < 2 || !L.adapters || L.r_max % 8 != 0 || L.S > kMetaSlots ||
+        L.n_items < kShrinkSplitMaxBlocks / 2)
+        return false;
+    for (int i = 0; i < L.n_slices; ++i) {
+        if (N[i] <= 0) return false;
+        gs[i] = gemm_bf16_plan(L.M, N[i], L.K);
+        if (gs[i].nsub != 0 || gs[i].tks > 1) return false;
+    }
+    return true;
+}
+
 hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm) {
     const int M = L.M, K = L.K, n = L.n_slices;
     if (M == 0 || n < 1) return hipSuccess;
@@ -595,6 +620,21 @@ hipError_t lora_forward_bf16(const LinearArgs& L, hipStream_t st, StageTimer* tm
     for (int i = 0; i < n; ++i) N[i] = L.slice[i].N;
     GemmPlan gj;
     if (n > 1 && joint_split(M, N, n, K, &gj)) return splitk_forward_bf16(L, gj, st, tm);
+    GemmPlan gs[kMaxSlices];
+    if (slices_share_shrink(L, N, gs)) {
+        ShrinkSlices ss{};
+        ss.n = n;
+        char* ws = static_cast<char*>(L.workspace);
+        for (int i = 0; i < n; ++i) {
+            ss.A_pool[i] = L.slice[i].A_pool;
+            ss.rank[i] = L.slice[i].rank;
+            ss.scale[i] = L.slice[i].scale;
+            ss.ext[i] = reinterpret_cast<uint16_t*>(ws + i * ext_stride(M, L.r_max));
+        }
+        hipError_t e = sgmv_shrink_slices(L.X, ss, L.token_order, L.work, L.n_items, K, L.r_max, st, tm);
+        for (int i = 0; i < n && e == hipSuccess; ++i) e = tiled_forward(L, L.slice[i], gs[i], st, tm, ss.ext[i]);
+        return e;
+    }
     for (int i = 0; i < n; ++i) {
         if (N[i] == 0) continue;
         const GemmPlan g = gemm_bf16_plan(M, N[i], K);

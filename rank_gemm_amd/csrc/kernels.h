@@ -100,6 +100,11 @@ hipError_t plan_device(const int32_t* ids, int T, int S, int cap, int32_t* plan,
 hipError_t sgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank,
                        const int32_t* token_order, const int32_t* work, int n_items, float* h, int K, int r_max,
                        hipStream_t st, StageTimer* tm, const float* scale = nullptr, uint16_t* ext = nullptr);
+// The expand operands of up to kMaxSlices projections over the same x in one
+// pass (x rows read once): slice i's A_pool, rank, scale and ext in ss.
+struct ShrinkSlices;
+hipError_t sgmv_shrink_slices(const uint16_t* X, const ShrinkSlices& ss, const int32_t* token_order,
+                              const int32_t* work, int n_items, int K, int r_max, hipStream_t st, StageTimer* tm);
 // The same over hs K ranges of hkc k each (few items, long K): fp32 planes in
 // part ([n_items * hs][16][r_max]), then h or ext as above.
 constexpr int kShrinkSplitMaxBlocks = 256;

@@ -40,6 +40,17 @@ __global__ __launch_bounds__(WAVES * 64) void shrink_bf16_kernel(const uint16_t*
     shrink_item<WAVES>(X, A_pool, r, token_order, it, out, K, 0, K, r_max, red);
 }
 
+// Several slices reading the same x: grid n_items, WAVES waves, the full K
+// range, each slice's expand operand written to its own ext.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void shrink_slices_kernel(const uint16_t* __restrict__ X, ShrinkSlices ss,
+                                                                   const int32_t* __restrict__ token_order,
+                                                                   const Item* __restrict__ work, int K, int r_max) {
+    __shared__ f32x4 red[WAVES * 4 * 64];
+    const Item it = work[blockIdx.x];
+    shrink_item_slices<WAVES>(X, ss, token_order, it, K, r_max, red);
+}
+
 // Few items: grid n_items * hs, block b = kz * n_items + item computes its
 // item over K range kz (hkc k, 4 waves) into its own 16-row plane of part
 // ([n_items * hs][16][r_max] fp32); shrink_finish_kernel adds the planes in
@@ -176,6 +187,17 @@ hipError_t sgmv_shrink(const uint16_t* X, const uint16_t* A_pool, const int32_t*
                       token_order, (const Item*)work, h, ext, K, r_max);
     return launch(tm, "sgmv_shrink", shrink_bf16_kernel<16>, dim3(n_items), dim3(1024), st, X, A_pool, rank, scale,
                   token_order, (const Item*)work, h, ext, K, r_max);
+}
+
+hipError_t sgmv_shrink_slices(const uint16_t* X, const ShrinkSlices& ss, const int32_t* token_order,
+                              const int32_t* work, int n_items, int K, int r_max, hipStream_t st, StageTimer* tm) {
+    static_assert(kShrinkMaxSlices == kMaxSlices, "slice tables");
+    if (n_items == 0) return hipSuccess;
+    if (n_items >= 256)
+        return launch(tm, "sgmv_shrink", shrink_slices_kernel<4>, dim3(n_items), dim3(256), st, X, ss, token_order,
+                      (const Item*)work, K, r_max);
+    return launch(tm, "sgmv_shrink", shrink_slices_kernel<16>, dim3(n_items), dim3(1024), st, X, ss, token_order,
+                  (const Item*)work, K, r_max);
 }
 
 hipError_t sgmv_shrink_split(const uint16_t* X, const uint16_t* A_pool, const int32_t* rank, const float* scale,

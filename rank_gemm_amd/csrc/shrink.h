@@ -121,4 +121,121 @@ __device__ __forceinline__ void shrink_item(const uint16_t* __restrict__ X, cons
     }
 }
 
+// The expand operands of several projections that read the same x (the
+// output slices of a merged gate/up or q/k/v, section "vLLM: preallocated
+// stacked buffers plus a Punica-style Triton kernel" of the page above): one
+// pass over the item's x rows feeds every slice's A rows. The 16-rank blocks
+// of all slices are taken in slice order, four at a time, each with its own
+// slice's A, rank mask, scale and output; a block's arithmetic is that of
+// shrink_item's, so each slice's operand is the same bit for bit.
+constexpr int kShrinkMaxSlices = 4;
+struct ShrinkSlices {
+    int n;
+    const uint16_t* A_pool[kShrinkMaxSlices];
+    const int32_t* rank[kShrinkMaxSlices];
+    const float* scale[kShrinkMaxSlices];
+    uint16_t* ext[kShrinkMaxSlices];  // [T][2][rp] each
+};
+
+template <int WAVES>
+__device__ __forceinline__ void shrink_item_slices(const uint16_t* __restrict__ X, const ShrinkSlices& ss,
+                                                   const int32_t* __restrict__ token_order, const Item& it, int K,
+                                                   int r_max, f32x4* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane & 15, kg = lane >> 4;
+    const bool valid = row < it.count;
+    const uint16_t* xp = X + (int64_t)token_order[it.begin + (valid ? row : 0)] * K;
+    const int rp = (r_max + 7) & ~7;
+    const int steps = (K + 31) >> 5;
+    const int per = (steps + WAVES - 1) / WAVES;
+    const int s_beg = wave * per, s_end = min(steps, s_beg + per);
+    // rank blocks per slice (uniform) and their running total
+    int nq[kShrinkMaxSlices], rs[kShrinkMaxSlices], total = 0;
+#pragma unroll
+    for (int i = 0; i < kShrinkMaxSlices; ++i) {
+        rs[i] = i < ss.n ? ss.rank[i][it.slot] : 0;
+        nq[i] = (rs[i] + 15) >> 4;
+        total += nq[i];
+    }
+    // global block b -> (slice, first rank of the block)
+    auto block_of = [&](int b, int& sl, int& q0) {
+        sl = 0;
+        q0 = 0;
+        int first = 0;
+#pragma unroll
+        for (int i = 0; i < kShrinkMaxSlices; ++i) {
+            if (b >= first && b < first + nq[i]) {
+                sl = i;
+                q0 = (b - first) * 16;
+            }
+            first += nq[i];
+        }
+    };
+    for (int g0 = 0; g0 < total; g0 += 4) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto run = [&](auto nb_tag) {
+            constexpr int NB = decltype(nb_tag)::value;
+            const uint16_t* aq[NB];
+            bool qok[NB];
+#pragma unroll
+            for (int qb = 0; qb < NB; ++qb) {
+                int sl, q0;
+                block_of(g0 + qb, sl, q0);
+                const int q = q0 + row;
+                qok[qb] = q < rs[sl];
+                aq[qb] = ss.A_pool[sl] + ((int64_t)it.slot * r_max + (qok[qb] ? q : 0)) * K;
+            }
+            constexpr int U = 4;
+            for (int s0 = s_beg; s0 < s_end; s0 += U) {
+                u32x4 a[U], b[U][NB];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int kk = (s0 + u) * 32 + kg * 8;
+                    const bool kin = (s0 + u) < s_end && kk < K;
+                    a[u] = *or_zero(valid && kin, xp + kk);
+#pragma unroll
+                    for (int qb = 0; qb < NB; ++qb) b[u][qb] = *or_zero(kin && qok[qb], aq[qb] + kk);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int qb = 0; qb < NB; ++qb) acc[qb] = mfma16x16x32(a[u], b[u][qb], acc[qb]);
+            }
+        };
+        switch (min(total - g0, 4)) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            default: run(std::integral_constant<int, 4>{}); break;
+        }
+        __syncthreads();  // red is reused across block groups
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) red[(wave * 4 + qb) * 64 + lane] = acc[qb];
+        __syncthreads();
+        // wave w finishes block g0 + w; lane holds rows 4 kg + e, column row
+        if (wave < 4 && g0 + wave < total) {
+            f32x4 v4 = red[wave * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) v4 += red[(w * 4 + wave) * 64 + lane];
+            int sl, q0;
+            block_of(g0 + wave, sl, q0);
+            const int q = q0 + row;
+            const float sc = ss.scale[sl][it.slot];
+            uint16_t* ext = ss.ext[sl];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = kg * 4 + e;
+                if (m >= it.count || q >= rp) continue;
+                const int64_t p = it.begin + m;
+                const float v = v4[e] * sc;
+                const uint16_t hi = f32_to_bf16(v);
+                ext[(p * 2) * rp + q] = hi;
+                ext[(p * 2 + 1) * rp + q] = f32_to_bf16(v - bf16_to_f32(hi));
+            }
+        }
+    }
+}
+
 }  // namespace lora

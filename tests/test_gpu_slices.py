@@ -127,6 +127,36 @@ def test_prefill_sized_slices_run_one_by_one():
     check_slices(w, ys, "prefill slices")
 
 
+@pytest.mark.parametrize("r_max,n_slices", [(16, 2), (32, 3)])
+def test_prefill_slices_share_one_shrink(r_max, n_slices):
+    """Slices that all take the tiled path, with enough work items, share one
+    shrink launch (x rows read once for every slice's A); each slice's output
+    equals, bit for bit, that of its own lora_linear call. Per-slice ranks
+    differ for the same slot (one slot is empty in one slice only, ranks not
+    multiples of 16), so a group of four rank blocks mixes slices."""
+    S = 9
+    g = np.random.default_rng(40 + r_max)
+    ranks = [[0] + [r_max] * 8]
+    ranks.append([0, 8, r_max, 0, 4, r_max, 12, r_max, 8])
+    ranks.append([0, 5, 16, r_max, 0, 24, r_max, 1, r_max])
+    ranks = [[min(r, r_max) for r in rr] for rr in ranks[:n_slices]]
+    alphas = [[2.0 * r for r in rr] for rr in ranks]
+    T = 4096
+    ids = np.repeat(g.integers(0, S, size=T // 256), 256).astype(np.int32)
+    d_outs = [2048, 1536, 1000][:n_slices]
+    w = make_slices(70 + r_max, T, 520, d_outs, S, ranks, alphas, ids, r_max=r_max)
+    ys, pools, stats = run_multi(w, profile=True)
+    assert stats["sgmv_shrink"]["count"] == 1 and stats["gemm_bf16"]["count"] == n_slices, stats
+    p = lora.plan(ids, S)
+    x = lora.to_device(w.projections[0].x, w.dtype)
+    for i, pr in enumerate(w.projections):
+        W = lora.to_device(pr.W, w.dtype)
+        y1 = lora.linear(x, W, pools[i], p)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, ys[i]), f"slice {i}: one shared shrink differs from the slice's own call"
+    check_slices(w, ys, f"shared shrink r_max={r_max}")
+
+
 def test_f32_slices():
     S = 5
     ranks = [[0, 8, 8, 8, 8], [0, 8, 0, 4, 8]]
