@@ -249,8 +249,12 @@ int lora_linear_device_plan(const lora_pool* pool, const void* x, const void* W,
  *   workspace    dev, at least lora_workspace_bytes_multi(slices, n, T) bytes
  * With bf16 pools, slices whose concatenated columns fall on the decode
  * (split-K) path are computed by one GEMM launch and one epilogue launch
- * between them, x being read once per K split for all slices; otherwise the
- * slices run one after another. No y may alias x, any W or another y.
+ * between them, x being read once per K split for all slices; otherwise each
+ * slice has its own GEMM launch, and when every slice takes the unsplit tiled
+ * path with the expand as extra K steps and the plan has at least 128 work
+ * items, one shrink launch serves all slices (x rows read once; each slice's
+ * output then equals its own lora_linear call bit for bit). No y may alias
+ * x, any W or another y.
  * Errors: LORA_EINVAL (n out of range, pools that differ, null pointer,
  * aliasing), LORA_ESPACE, LORA_EHIP.
  */
