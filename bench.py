@@ -218,7 +218,7 @@ def headline(args, torch, np, lora, acc, w3):
     ach = gemm_fl / (t_gemm * 1e-6) / 1e12
     roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("gemm_tile_kernel<256, 256, 2, 2, 2, false, false, false>", "traffic_prefill_gate_up.json",
+            "traffic": measured_traffic("gemm_tile_kernel<256, 256, 2, 2, 2, false, false, false, true>", "traffic_prefill_gate_up.json",
                                         ("gemm_bf16.hip", "fuse.h", "common.h", "kernels.h")),
             "traffic_note": "bytes per launch between the L2s and the memory fabric (MALL/HBM): FETCH_SIZE x 2.0 + "
                             "WRITE_SIZE x 1.0 (a plain 256 MiB copy reads those factors), against 416 MB of "

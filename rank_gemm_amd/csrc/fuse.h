@@ -339,6 +339,20 @@ __device__ __forceinline__ void dma16(gptr<u32x4> src, u32x4* lds_dst) {
 __device__ __forceinline__ void dma16_nt(gptr<u32x4> src, u32x4* lds_dst) {
     __builtin_amdgcn_global_load_lds((gptr<void>)src, (lds_void_ptr)lds_dst, 16, 0, 2);
 }
+// A raw buffer resource over [p, p + bytes) (bytes < 2^31): a load whose
+// per-lane offset is at or past its end returns zeros without touching
+// memory. The same direct-to-LDS load through it takes a 32-bit per-lane byte
+// offset and a uniform one (soff, not range-checked), so a tile's row offsets
+// are set once and each step only moves soff: no per-step address arithmetic
+// per lane, and half the address registers of 64-bit pointers.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a per-lane offset past every resource
+__device__ __forceinline__ brsrc make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bdma16(brsrc r, uint32_t voff, uint32_t soff, u32x4* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_dst, 16, (int)voff, (int)soff, 0, 0);
+}
 __device__ __forceinline__ uint32_t lds_offset(const u32x4* p) { return (uint32_t)(uintptr_t)(lds_u32x4_ptr)p; }
 
 template <int OFF>

@@ -132,11 +132,17 @@ struct SplitOut {
 // phase B. With NS >= 3, step kt + NS - 1 is loaded during step kt into the
 // buffer of step kt - 1 (every wave finished reading it before step kt - 1's
 // barrier), so its loads are spread over both phases.
-template <int BM, int BN, int WM, int WN, int NS, bool EPI, bool KTAIL, bool SPLIT>
+// BUF: loads through buffer resources (x, the tile's W rows, ext, B_pool; the
+// host takes this form when each is under 2 GiB): per-lane row offsets set
+// once per tile, the base step's k in the uniform offset. Otherwise 64-bit
+// addresses, moved by k every step (8192 x 4096 -> 14336: 737-747 us against
+// 750-757 us, interleaved on one box, identical outputs).
+template <int BM, int BN, int WM, int WN, int NS, bool EPI, bool KTAIL, bool SPLIT, bool BUF>
 __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_tile_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, Fuse f, SplitOut so) {
     static_assert(!(SPLIT && EPI), "a split runs no expand");
+    static_assert(!(SPLIT && BUF), "splits take 64-bit addresses");
     constexpr int BK = 64, NW = WM * WN;
     constexpr int FI = BM / WM / 16, FJ = BN / WN / 16;    // MFMA blocks of a wave
     constexpr int DA = BM / 8 / NW, DB = BN / 8 / NW, ND = DA + DB;  // load instructions of a wave per step
@@ -181,6 +187,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
         ncol[b] = n0 + (u >> 3) * 64 + (u & 7) + 8 * rl;
         bp[b] = W + (int64_t)min(ncol[b], N - 1) * K + kb + (cl ^ (u & 7)) * 8;
     }
+    // the buffer form's resources and this lane's byte offsets of its rows
+    const brsrc rX = make_rsrc(X, (uint32_t)M * (uint32_t)K * 2u);
+    const brsrc rW = make_rsrc(W + (int64_t)n0 * K, (uint32_t)(min(N, n0 + BN) - n0) * (uint32_t)K * 2u);
+    const brsrc rE = make_rsrc(f.ext, (uint32_t)M * (uint32_t)f.rp * 4u);
+    const brsrc rB = make_rsrc(f.B_pool, (uint32_t)f.S * (uint32_t)N * (uint32_t)f.r_max * 2u);
+    uint32_t aoff[DA], boff[DB];
+    if constexpr (BUF) {
+#pragma unroll
+        for (int b = 0; b < DA; ++b)
+            aoff[b] = (uint32_t)(f.token_order[min(prow[b], M - 1)] * K + (cl ^ ((wave * DA + b) & 7)) * 8) * 2u;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+            boff[b] = (uint32_t)((min(ncol[b], N - 1) - n0) * K + (cl ^ ((wave * DB + b) & 7)) * 8) * 2u;
+    }
+    uint32_t vsrc[ND];  // buffer form: per-lane offsets of an extra step, or of a K-tail base step
+    uint32_t soff = 0;  // buffer form: the base step's k, in bytes
     __syncthreads();  // slot metadata staged
     // the expand's extra steps; in a split, split kz takes extra steps kz,
     // kz + ks, kz + 2 ks, ... of the tile (the partials carry the correction)
@@ -198,6 +220,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     // lane cl fetches chunk cl ^ (u % 8) with load instruction u
     auto sources_base = [&](int kt) {
         const int k = (kt - ne) * BK;
+        if constexpr (BUF) {
+            soff = (uint32_t)k * 2u;
+            if constexpr (KTAIL) {
+#pragma unroll
+                for (int b = 0; b < DA; ++b)
+                    vsrc[b] = k + (cl ^ ((wave * DA + b) & 7)) * 8 < Kr ? aoff[b] : kOutOfRange;
+#pragma unroll
+                for (int b = 0; b < DB; ++b)
+                    vsrc[DA + b] = k + (cl ^ ((wave * DB + b) & 7)) * 8 < Kr ? boff[b] : kOutOfRange;
+            }
+            return;
+        }
 #pragma unroll
         for (int b = 0; b < DA; ++b) {
             const bool kin = !KTAIL || k + (cl ^ ((wave * DA + b) & 7)) * 8 < Kr;
@@ -218,6 +252,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     };
     auto sources_extra = [&](int kt) {
         const ExtraStepMeta xm = extra_step(xs, lmeta, wlist, kz + ks * kt);  // the tile's step of this split
+        if constexpr (BUF) {
+#pragma unroll
+            for (int b = 0; b < DA; ++b) {
+                const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DA + b) & 7), f.rp);
+                vsrc[b] = c.ok && prow[b] >= c.sb && prow[b] < c.se ? (uint32_t)(prow[b] * 2 * f.rp + c.k) * 2u
+                                                                    : kOutOfRange;
+            }
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DB + b) & 7), f.rp);
+                vsrc[DA + b] =
+                    c.ok && ncol[b] < N ? (uint32_t)((c.s * N + ncol[b]) * f.r_max + c.q) * 2u : kOutOfRange;
+            }
+            return;
+        }
 #pragma unroll
         for (int b = 0; b < DA; ++b) {
             const ExtraChunk c = extra_chunk(xs, xm, cl ^ ((wave * DA + b) & 7), f.rp);
@@ -229,10 +278,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
             src[DA + b] = or_zero(c.ok && ncol[b] < N, f.B_pool + ((int64_t)c.s * N + ncol[b]) * f.r_max + c.q);
         }
     };
-    auto load_piece = [&](int g, int buf) {
+    // XN: the loads are of an extra step (in the buffer form: ext and B_pool
+    // with per-lane offsets; else x and W)
+    auto load_piece = [&](int g, int buf, auto xn_tag) {
+        constexpr bool XN = decltype(xn_tag)::value;
         const int u = g < DA ? wave * DA + g : wave * DB + (g - DA);
-        dma16(src[g], lds + buf * STAGE + ((g < DA ? 0 : ABYTES) + (u >> 3) * kGroupBytes + (u & 7) * kInstrBytes) / 16);
+        u32x4* dst = lds + buf * STAGE + ((g < DA ? 0 : ABYTES) + (u >> 3) * kGroupBytes + (u & 7) * kInstrBytes) / 16;
+        if constexpr (BUF) {
+            if constexpr (XN) bdma16(g < DA ? rE : rB, vsrc[g], 0u, dst);
+            else bdma16(g < DA ? rX : rW, KTAIL ? vsrc[g] : (g < DA ? aoff[g] : boff[g - DA]), soff, dst);
+        } else {
+            dma16(src[g], dst);
+        }
     };
+    using XT = std::true_type;
+    using XF = std::false_type;
     const int fr = lane & 15, fc = lane >> 4;
     const uint32_t lane_off = lds_offset(lds) + (fr & 7) * kInstrBytes + (fr >> 3) * 128;
     uint32_t abase[2], bbase[2];
@@ -251,10 +311,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     // steps 0 .. L - 1 in flight, step 0 landed, its first half read
 #pragma unroll
     for (int s0 = 0; s0 < L; ++s0) {
-        if (s0 < ne) sources_extra(s0);
-        else sources_base(min(s0, nt - 1));
+        if (s0 < ne) {
+            sources_extra(s0);
 #pragma unroll
-        for (int g = 0; g < ND; ++g) load_piece(g, s0);
+            for (int g = 0; g < ND; ++g) load_piece(g, s0, XT{});
+        } else {
+            sources_base(min(s0, nt - 1));
+#pragma unroll
+            for (int g = 0; g < ND; ++g) load_piece(g, s0, XF{});
+        }
     }
     vm_landed<(L - 1) * ND>();
     stage_barrier();
@@ -272,7 +337,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     // one step; `next` sets the sources of step kt + L, loaded into buffer bn
     // (step kt's own buffer with 2 stages: only after every wave has read it)
     int bc = 0, bn = L % NS;  // buffers of step kt and of step kt + L
-    auto step = [&](int kt, auto&& next) {
+    auto step = [&](int kt, auto&& next, auto xn_tag) {
         const uint32_t so = bc * STAGE * 16, sn = (bc + 1 == NS ? 0 : bc + 1) * STAGE * 16;
         next(kt + L);
         frags_landed(A0);
@@ -284,7 +349,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
             read_half(gc, A1, B1, abase[1] + so, bbase[1] + so);
             static_for(std::make_integer_sequence<int, ND>{}, [&](auto pc) {  // loads of this group
                 constexpr int pi = decltype(pc)::v;
-                if constexpr (pi < NDA && pi * NR / NDA == g) load_piece(pi, bn);
+                if constexpr (pi < NDA && pi * NR / NDA == g) load_piece(pi, bn, xn_tag);
             });
             static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {  // MFMAs of this group
                 constexpr int t = decltype(tc)::v;
@@ -304,7 +369,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
             read_half(gc, A0, B0, abase[0] + sn, bbase[0] + sn);
             static_for(std::make_integer_sequence<int, ND>{}, [&](auto pc) {
                 constexpr int pi = decltype(pc)::v;
-                if constexpr (pi >= NDA && (pi - NDA) * NR / NDB == g) load_piece(pi, bn);
+                if constexpr (pi >= NDA && (pi - NDA) * NR / NDB == g) load_piece(pi, bn, xn_tag);
             });
             static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {
                 constexpr int t = decltype(tc)::v;
@@ -319,8 +384,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     // steps whose step kt + L is an extra step, then the rest (the last L
     // steps reload the last step: the load count per step stays fixed)
     int kt = 0;
-    for (; kt + L < ne; ++kt) step(kt, sources_extra);
-    for (; kt < nt; ++kt) step(kt, [&](int s) { sources_base(min(s, nt - 1)); });
+    for (; kt + L < ne; ++kt) step(kt, sources_extra, XT{});
+    for (; kt < nt; ++kt) step(kt, [&](int s) { sources_base(min(s, nt - 1)); }, XF{});
     frags_landed(A0);
     frags_landed(B0);
     vm_landed<0>();
@@ -479,25 +544,44 @@ size_t gemm_bf16_workspace(int M, const int* N, int n_slices, int K, int r_max) 
     return need;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool SPLIT_OK>
+// Whether every buffer the tile kernel's buffer form reads fits a buffer
+// resource (under 2 GiB, so per-lane byte offsets and the out-of-range offset
+// stay apart): x, one tile's W rows, ext, B_pool.
+static bool buffers_fit(int M, int N, int K, int BN, const Fuse& f) {
+    const int64_t lim = int64_t(1) << 31;
+    return (int64_t)M * K * 2 < lim && (int64_t)BN * K * 2 < lim && (int64_t)M * f.rp * 4 < lim &&
+           (int64_t)f.S * N * f.r_max * 2 < lim;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, bool SPLIT_OK, bool BUF_OK = false>
 static hipError_t launch_tile(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int N, int K, const Fuse& f,
                             bool epi, hipStream_t st, StageTimer* tm, const SplitOut& so = SplitOut{}, int ks = 1) {
     const int tiles_m = cdiv(M, BM), tiles_n = cdiv(N, BN);
     const bool ktail = K % 64 != 0;
     const dim3 block(64 * WM * WN);
-    decltype(&gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, false>) ker;
+    decltype(&gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, false, false>) ker;
     if constexpr (SPLIT_OK) {
         if (so.part) {
-            ker = ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, false, true, true>
-                        : gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, true>;
+            ker = ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, false, true, true, false>
+                        : gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, true, false>;
             return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n * ks), block, st, X, W, Y, M, N, K, tiles_m,
                           tiles_n, f, so);
         }
     }
-    ker = epi ? (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, true, true, false>
-                       : gemm_tile_kernel<BM, BN, WM, WN, NS, true, false, false>)
-              : (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, false, true, false>
-                       : gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, false>);
+    bool buf = false;
+    if constexpr (BUF_OK) buf = buffers_fit(M, N, K, BN, f);
+    if (buf) {
+        if constexpr (BUF_OK)
+            ker = epi ? (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, true, true, false, true>
+                               : gemm_tile_kernel<BM, BN, WM, WN, NS, true, false, false, true>)
+                      : (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, false, true, false, true>
+                               : gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, false, true>);
+    } else {
+        ker = epi ? (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, true, true, false, false>
+                           : gemm_tile_kernel<BM, BN, WM, WN, NS, true, false, false, false>)
+                  : (ktail ? gemm_tile_kernel<BM, BN, WM, WN, NS, false, true, false, false>
+                           : gemm_tile_kernel<BM, BN, WM, WN, NS, false, false, false, false>);
+    }
     return launch(tm, "gemm_bf16", ker, dim3(tiles_m * tiles_n), block, st, X, W, Y, M, N, K, tiles_m, tiles_n, f,
                   SplitOut{});
 }
@@ -591,7 +675,7 @@ static hipError_t tiled_forward(const LinearArgs& L, const SliceArgs& sl, const 
         if (e != hipSuccess) return e;
     }
     const bool epi = L.adapters && !f.ext;
-    if (g.bm == 256 && g.bn == 256) return launch_tile<256, 256, 2, 2, 2, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
+    if (g.bm == 256 && g.bn == 256) return launch_tile<256, 256, 2, 2, 2, false, true>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     if (g.bm == 256) return launch_tile<256, 128, 4, 2, 3, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     if (g.bm == 128) return launch_tile<128, 128, 2, 4, 3, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);
     return launch_tile<64, 128, 2, 4, 4, false>(L.X, sl.W, sl.Y, M, N, K, f, epi, st, tm);

@@ -442,10 +442,13 @@ def test_pool_layout_and_slot0():
 
 
 # ------------------------------------------------------------ long context --
-def test_row_offsets_beyond_int32():
+@pytest.mark.parametrize("d_out", [32, 512])
+def test_row_offsets_beyond_int32(d_out):
     """T * d_in > 2^31 elements: rows past 524,288 of a 4096-wide x are read
-    and written at 64-bit offsets (the long-context overflow hazard)."""
-    T, d_in, d_out, S = 524_288 + 640, 4096, 32, 3
+    and written at 64-bit offsets (the long-context overflow hazard). At
+    d_out = 32 the GEMM takes 256 x 128 tiles; at 512, 256 x 256 tiles, whose
+    x is then too large for a buffer resource (the 64-bit address form)."""
+    T, d_in, S = 524_288 + 640, 4096, 3
     ids = np.zeros(T, np.int32)
     tail = np.arange(T - 40, T)
     ids[tail[:20]] = 1
