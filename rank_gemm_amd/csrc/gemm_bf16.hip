@@ -336,8 +336,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
     };
     // one step; `next` sets the sources of step kt + L, loaded into buffer bn
     // (step kt's own buffer with 2 stages: only after every wave has read it)
-    int bc = 0, bn = L % NS;  // buffers of step kt and of step kt + L
-    auto step = [&](int kt, auto&& next, auto xn_tag) {
+    // bcv: the buffer of step kt (kt % NS), a run-time int or a constant
+    auto step = [&](int kt, auto&& next, auto xn_tag, auto bcv) {
+        int bc;
+        if constexpr (std::is_integral_v<decltype(bcv)>) bc = bcv;
+        else bc = decltype(bcv)::v;
+        const int bn = bc + L >= 2 * NS ? bc + L - 2 * NS : bc + L >= NS ? bc + L - NS : bc + L;  // step kt + L's
         const uint32_t so = bc * STAGE * 16, sn = (bc + 1 == NS ? 0 : bc + 1) * STAGE * 16;
         next(kt + L);
         frags_landed(A0);
@@ -378,14 +382,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
         });
         __builtin_amdgcn_sched_barrier(0);
         frags_retire(A1, B1);
-        bc = bc + 1 == NS ? 0 : bc + 1;
-        bn = bn + 1 == NS ? 0 : bn + 1;
     };
     // steps whose step kt + L is an extra step, then the rest (the last L
-    // steps reload the last step: the load count per step stays fixed)
-    int kt = 0;
-    for (; kt + L < ne; ++kt) step(kt, sources_extra, XT{});
-    for (; kt < nt; ++kt) step(kt, [&](int s) { sources_base(min(s, nt - 1)); }, XF{});
+    // steps reload the last step: the load count per step stays fixed). The
+    // base steps run NS to an iteration, so that their buffers, and with them
+    // every LDS address of the step, are constants.
+    int kt = 0, bcr = 0;  // bcr = kt % NS
+    auto adv = [&] { bcr = bcr + 1 == NS ? 0 : bcr + 1; };
+    auto base_next = [&](int s) { sources_base(min(s, nt - 1)); };
+    for (; kt + L < ne; ++kt, adv()) step(kt, sources_extra, XT{}, bcr);
+    for (; kt < nt && bcr != 0; ++kt, adv()) step(kt, base_next, XF{}, bcr);
+    for (; kt + NS <= nt; kt += NS)
+        static_for(std::make_integer_sequence<int, NS>{}, [&](auto sc) { step(kt + decltype(sc)::v, base_next, XF{}, sc); });
+    for (; kt < nt; ++kt, adv()) step(kt, base_next, XF{}, bcr);
     frags_landed(A0);
     frags_landed(B0);
     vm_landed<0>();
