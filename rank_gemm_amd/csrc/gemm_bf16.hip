@@ -346,18 +346,27 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
         next(kt + L);
         frags_landed(A0);
         frags_landed(B0);
-        // phase A: MFMAs of the first half, reads of the second half
+        // phase A: MFMAs of the first half, reads of the second half. In a
+        // group, the fragment read follows the group's first MFMA and its
+        // loads the second, so that each waits in an MFMA's shadow.
         static_for(std::make_integer_sequence<int, NR>{}, [&](auto gc) {
             constexpr int g = decltype(gc)::v;
+            constexpr int t0 = (g * NM + NR - 1) / NR, t1 = ((g + 1) * NM + NR - 1) / NR;  // this group's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (t0 < t1) mfma(acc[t0 / FJ][t0 % FJ], A0[t0 / FJ], B0[t0 % FJ]);
             __builtin_amdgcn_sched_barrier(0);
             read_half(gc, A1, B1, abase[1] + so, bbase[1] + so);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (t0 + 1 < t1) mfma(acc[(t0 + 1) / FJ][(t0 + 1) % FJ], A0[(t0 + 1) / FJ], B0[(t0 + 1) % FJ]);
+            __builtin_amdgcn_sched_barrier(0);
             static_for(std::make_integer_sequence<int, ND>{}, [&](auto pc) {  // loads of this group
                 constexpr int pi = decltype(pc)::v;
                 if constexpr (pi < NDA && pi * NR / NDA == g) load_piece(pi, bn, xn_tag);
             });
-            static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {  // MFMAs of this group
+            __builtin_amdgcn_sched_barrier(0);
+            static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {  // the group's other MFMAs
                 constexpr int t = decltype(tc)::v;
-                if constexpr (t * NR / NM == g) mfma(acc[t / FJ][t % FJ], A0[t / FJ], B0[t % FJ]);
+                if constexpr (t >= t0 + 2 && t < t1) mfma(acc[t / FJ][t % FJ], A0[t / FJ], B0[t % FJ]);
             });
         });
         __builtin_amdgcn_sched_barrier(0);
@@ -369,15 +378,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) __attribute__((amdgpu_waves_per_eu
         // phase B: MFMAs of the second half, reads of step kt + 1's first half, the other loads
         static_for(std::make_integer_sequence<int, NR>{}, [&](auto gc) {
             constexpr int g = decltype(gc)::v;
+            constexpr int t0 = (g * NM + NR - 1) / NR, t1 = ((g + 1) * NM + NR - 1) / NR;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (t0 < t1) mfma(acc[t0 / FJ][t0 % FJ], A1[t0 / FJ], B1[t0 % FJ]);
             __builtin_amdgcn_sched_barrier(0);
             read_half(gc, A0, B0, abase[0] + sn, bbase[0] + sn);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (t0 + 1 < t1) mfma(acc[(t0 + 1) / FJ][(t0 + 1) % FJ], A1[(t0 + 1) / FJ], B1[(t0 + 1) % FJ]);
+            __builtin_amdgcn_sched_barrier(0);
             static_for(std::make_integer_sequence<int, ND>{}, [&](auto pc) {
                 constexpr int pi = decltype(pc)::v;
                 if constexpr (pi >= NDA && (pi - NDA) * NR / NDB == g) load_piece(pi, bn, xn_tag);
             });
+            __builtin_amdgcn_sched_barrier(0);
             static_for(std::make_integer_sequence<int, NM>{}, [&](auto tc) {
                 constexpr int t = decltype(tc)::v;
-                if constexpr (t * NR / NM == g) mfma(acc[t / FJ][t % FJ], A1[t / FJ], B1[t % FJ]);
+                if constexpr (t >= t0 + 2 && t < t1) mfma(acc[t / FJ][t % FJ], A1[t / FJ], B1[t % FJ]);
             });
         });
         __builtin_amdgcn_sched_barrier(0);
