@@ -78,16 +78,16 @@ def parse():
                     help="only the headline steps (for profiler passes: no side figures, no oracle)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode-step figures (for profiler passes; the line's value is then null)")
-    ap.add_argument("--crossover", action="store_true",
-                    help="also time the SGMV correction against the BGMV correction over ranks, adapters and "
+    ap.add_argument("--no-crossover", action="store_true",
+                    help="skip timing the SGMV correction against the BGMV correction over ranks, adapters and "
                          "tokens per adapter")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 256 MiB device copies (reference for the FETCH_SIZE/WRITE_SIZE counters)")
     a = ap.parse_args()
     if a.headline_only:
-        a.no_cpu_baseline = a.no_decode = a.no_slices = a.no_configs = a.no_library = True
+        a.no_cpu_baseline = a.no_decode = a.no_slices = a.no_configs = a.no_library = a.no_crossover = True
     if a.decode_only:
-        a.no_cpu_baseline = a.no_slices = a.no_configs = a.no_library = True
+        a.no_cpu_baseline = a.no_slices = a.no_configs = a.no_library = a.no_crossover = True
     return a
 
 
@@ -591,6 +591,49 @@ def correction_crossover(torch, np, lora, K=4096, N=4096):
     return rows
 
 
+def ceilings(torch):
+    """What library kernels reach on this machine, as reproducible reference
+    points for the rooflines: a plain device-to-device copy of 1 GiB (read +
+    write bytes per second) and hipBLASLt's bf16 GEMM at 8192 x 8192 x 8192 in
+    the base product's layout, each timed with stream events, best of 3
+    rounds."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_us(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(3):
+            ev0.record()
+            for _ in range(n):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            t.append(ev0.elapsed_time(ev1) / n * 1e3)
+        return min(t)
+
+    src = torch.empty(2**30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    cp_us = best_us(lambda: dst.copy_(src))
+    del src, dst
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    mm_us = best_us(lambda: torch.nn.functional.linear(a, b, out=c), 5)
+    del a, b, c
+    torch.cuda.empty_cache()
+    out = {"hbm_copy": {"bytes": 2 * 2**30, "us": round(cp_us, 1), "tbps": round(2 * 2**30 / cp_us / 1e6, 3),
+                        "frac_of_8tbps": round(2 * 2**30 / cp_us / 1e3 / HBM_PEAK_GBS, 4),
+                        "note": "torch device-to-device copy of 1 GiB; read + write bytes"},
+           "library_gemm": {"shape": "8192 x 8192 x 8192 bf16", "us": round(mm_us, 1),
+                            "tflops": round(2 * 8192**3 / mm_us / 1e6, 1),
+                            "frac_of_peak": round(2 * 8192**3 / mm_us / 1e6 / BF16_PEAK_TFLOPS, 4),
+                            "note": "torch.nn.functional.linear (hipBLASLt), x [M, K] times W [N, K] transposed, "
+                                    "the layout of the base product"}}
+    log(f"ceilings {out}")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -619,7 +662,8 @@ def main():
 
     dec = None if args.no_decode else decode_step(args, torch, np, lora, acc, make_config, make_qkv_decode)
     others = None if args.no_configs else other_configs(args, torch, np, lora, acc, make_config)
-    crossover = correction_crossover(torch, np, lora) if args.crossover else None
+    crossover = None if args.no_crossover else correction_crossover(torch, np, lora)
+    ceil = None if (args.no_library or args.no_configs) else ceilings(torch)
 
     if args.copy_calibration:
         src = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -647,6 +691,7 @@ def main():
         "roofline": roof, "cpu_baseline": cpu,
         "call": call, "kernels": kstats(hstats), "base_only": base,
         "decode": dec, "other_configs": others, "cpu_oracle": cpu_table, "correction_crossover": crossover,
+        "ceilings": ceil,
     }
     print(json.dumps(out), flush=True)
 
