@@ -169,6 +169,24 @@ int lora_plan_chunked(int S, const int32_t* slot_ids, int T, int chunk, int32_t*
                       int32_t* slot_indptr, int32_t* work, int work_cap, lora_plan_info* info);
 
 /*
+ * Copy a plan (or any int32 buffer) from pinned host memory to the device
+ * with one kernel on `stream` that reads the host buffer in place over the
+ * bus. The plan is rebuilt on the host every step and read by every layer
+ * ("LoRA serving, embeddings, rerankers, pooling", mlinterviewnotes.com,
+ * worked example in section "LoRA and speculative decoding"); copied this
+ * way its upload is ordered on the compute stream like any kernel, instead
+ * of waiting for a copy engine between two kernels.
+ *   host_plan  host int32 [words], pinned (hipHostMalloc, or torch's
+ *              pin_memory); caller-owned; read when the stream reaches this
+ *              call, so it must not be rewritten before then (record an
+ *              event after the call and wait on it)
+ *   dev_plan   dev int32 [words], caller-owned
+ * Errors: LORA_EINVAL (null pointers; a host buffer the GPU cannot read,
+ * i.e. not pinned), LORA_EHIP. words == 0 launches nothing.
+ */
+int lora_plan_upload(const int32_t* host_plan, int32_t* dev_plan, size_t words, void* stream);
+
+/*
  * The same plan built on the device, for steps captured in a HIP graph (no
  * host work, no host-to-device copy, no allocation, one kernel). Launch
  * overhead is what drives engines to fixed-size buffers and graph capture

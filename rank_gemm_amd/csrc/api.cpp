@@ -321,6 +321,20 @@ size_t lora_plan_device_words(int T, int S) {
     return 4 * (size_t)cap + (size_t)T + (size_t)S + 1 + 8;
 }
 
+int lora_plan_upload(const int32_t* host_plan, int32_t* dev_plan, size_t words, void* stream) {
+    if (words == 0) return LORA_OK;
+    if (!host_plan || !dev_plan) return LORA_EINVAL;
+    // the device's address of the pinned buffer (fails for pageable memory)
+    void* src = nullptr;
+    if (hipHostGetDevicePointer(&src, const_cast<int32_t*>(host_plan), 0) != hipSuccess || !src) {
+        (void)hipGetLastError();
+        return LORA_EINVAL;
+    }
+    return lora::plan_upload(static_cast<const int32_t*>(src), dev_plan, words, as_stream(stream)) == hipSuccess
+               ? LORA_OK
+               : LORA_EHIP;
+}
+
 int lora_plan_device(int S, const int32_t* slot_ids, int T, int32_t* plan, void* stream) {
     if (S < 1 || S > LORA_DEVICE_PLAN_MAX_SLOTS || T < 0 || !plan || (T > 0 && !slot_ids)) return LORA_EINVAL;
     const int cap = std::max(lora_plan_max_items(T, S), 1);

@@ -92,6 +92,7 @@ hipError_t generic_linear(int dtype, const void* X, const void* W, void* Y, cons
 // to cap with empty items on slot 0; one workgroup.
 constexpr int kDevPlanMaxSlots = 4096;
 hipError_t plan_device(const int32_t* ids, int T, int S, int cap, int32_t* plan, hipStream_t st);
+hipError_t plan_upload(const int32_t* src, int32_t* dst, size_t words, hipStream_t st);
 
 // ---- SGMV shrink (bf16, K % 8 == 0) --------------------------------------------
 // h: fp32 [T][r_max] indexed by sorted position (rows of adapter items only).

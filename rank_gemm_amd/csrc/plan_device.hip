@@ -11,6 +11,8 @@
 // ballots. The work list is padded to its capacity with empty items on slot
 // 0 (rank 0), which every kernel skips, so launches sized for the capacity
 // need no host knowledge of the plan.
+#include <algorithm>
+
 #include "../../include/lora.h"
 #include "common.h"
 #include "kernels.h"
@@ -159,7 +161,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
     }
 }
 
+// Copy of a pinned host buffer: 16-byte pieces when both ends allow, then
+// the tail words.
+__global__ __launch_bounds__(256) void plan_upload_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst,
+                                                          size_t words, int vec) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t n4 = vec ? words / 4 : 0;
+    if (i < n4) reinterpret_cast<int4*>(dst)[i] = reinterpret_cast<const int4*>(src)[i];
+    const size_t t = 4 * n4 + i;
+    if (t < words && i < (vec ? 4 : words)) dst[t] = src[t];
+}
+
 }  // namespace
+
+hipError_t plan_upload(const int32_t* src, int32_t* dst, size_t words, hipStream_t st) {
+    if (words == 0) return hipSuccess;
+    const int vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+    const size_t n = vec ? std::max<size_t>(words / 4, 4) : words;
+    return launch(nullptr, "plan_upload", plan_upload_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, src, dst,
+                  words, vec);
+}
 
 hipError_t plan_device(const int32_t* ids, int T, int S, int cap, int32_t* plan, hipStream_t st) {
     return launch(nullptr, "plan_device", plan_device_kernel, dim3(1), dim3(kPlanThreads), st, ids, T, S, cap, plan);

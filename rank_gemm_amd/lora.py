@@ -31,7 +31,7 @@ EXPORTS = (
     "lora_status_string", "lora_profile_begin", "lora_profile_end", "lora_workspace_bytes_multi",
     "lora_linear_multi", "lora_plan_device_words", "lora_plan_device", "lora_linear_device_plan",
     "lora_shrink_bgmv", "lora_linear_multi_device_plan", "lora_plan_chunked", "lora_delta", "lora_delta_bgmv",
-    "lora_linear_noalloc",
+    "lora_linear_noalloc", "lora_plan_upload",
 )
 LORA_DEVICE_PLAN_MAX_SLOTS = 4096
 LORA_NOALLOC_MAX_WORKSPACE = 32 << 20
@@ -97,6 +97,7 @@ def lib():
             L.lora_plan_device_words.argtypes = [_I, _I]
             L.lora_plan_device_words.restype = _SZ
             L.lora_plan_device.argtypes = [_I, _P, _I, _P, _P]
+            L.lora_plan_upload.argtypes = [_P, _P, _SZ, _P]
             L.lora_linear_device_plan.argtypes = [_P, _P, _P, _P, _I, _P, _P, _SZ, _P]
             L.lora_linear_multi_device_plan.argtypes = [ctypes.POINTER(SliceDesc), _I, _P, _P, _I, _P, _SZ, _P]
             L.lora_shrink_bgmv.argtypes = [_P, _P, _P, _I, _P, _P, _SZ, _P]
@@ -281,7 +282,8 @@ def plan(slot_ids, S: int, device="cuda", upload: bool = True, chunk: int = LORA
     if upload:
         _require_gpu()
         dev = torch.empty(total, dtype=torch.int32, device=device)
-        dev.copy_(host, non_blocking=True)
+        with torch.cuda.device(dev.device):
+            _check(lib().lora_plan_upload(base, dev.data_ptr(), total, _stream(dev.device)), "lora_plan_upload")
     p = Plan(int(S), T, info, host, dev, n_work, int(chunk))
     if upload:
         # the staging buffers of plan_into, allocated now rather than on
@@ -302,7 +304,8 @@ def plan_into(p: Plan, slot_ids) -> Plan:
 
     The plan is written into one of two pinned staging buffers that the plan
     owns for its lifetime (the first is the buffer lora_plan filled), in
-    turn, and copied from there on the current stream. Before a staging
+    turn, and copied from there on the current stream by lora_plan_upload
+    (a kernel reading the pinned buffer in place). Before a staging
     buffer is written again, the host waits for the copy that last read it
     (two plans back). No pinned memory is allocated here: registering new
     host memory with the GPU stalls the kernels running at that moment."""
@@ -323,7 +326,9 @@ def plan_into(p: Plan, slot_ids) -> Plan:
     _check(lib().lora_plan_chunked(int(p.S), ids.ctypes.data, p.T, p.chunk, base + 16 * p._n_work,
                                    base + 4 * (4 * p._n_work + p.T), base, p._n_work, ctypes.byref(info)),
            "lora_plan_chunked")
-    p.dev.copy_(host, non_blocking=True)
+    with torch.cuda.device(p.dev.device):
+        _check(lib().lora_plan_upload(base, p.dev.data_ptr(), int(p.dev.numel()), _stream(p.dev.device)),
+               "lora_plan_upload")
     p._ev[k].record()
     p.host, p.info = host, info
     return p

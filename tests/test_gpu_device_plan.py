@@ -201,3 +201,42 @@ def test_multi_slice_over_device_plan_in_a_graph():
         torch.cuda.synchronize()
         for i in range(3):
             assert torch.equal(ys[i].view(torch.int16), want[i].view(torch.int16)), f"assignment {rep} slice {i}"
+
+
+@pytest.mark.parametrize("words", [1, 3, 4, 5, 1027, 40_013])
+def test_plan_upload_kernel(words):
+    """lora_plan_upload copies a pinned host buffer bit for bit, at word
+    counts that take the 16-byte path with and without tail words and the
+    word path (an unaligned source); pageable host memory is refused."""
+    L = lora.lib()
+    g = np.random.default_rng(words)
+    host = torch.from_numpy(g.integers(-2**31, 2**31 - 1, size=words + 1, dtype=np.int64).astype(np.int32)).pin_memory()
+    for off in (0, 1):  # off = 1: a source 4 bytes past 16-byte alignment
+        n = words - off if words > off else words
+        dev = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        rc = L.lora_plan_upload(host.data_ptr() + 4 * off, dev.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+        assert rc == lora.LORA_OK
+        torch.cuda.synchronize()
+        assert torch.equal(dev.cpu(), host[off:off + n])
+    pageable = np.arange(words, dtype=np.int32)
+    dev = torch.empty(words, dtype=torch.int32, device="cuda")
+    assert L.lora_plan_upload(pageable.ctypes.data, dev.data_ptr(), words, None) == lora.LORA_EINVAL
+
+
+def test_plan_into_steps_follow_new_ids():
+    """plan_into over many steps (the two pinned staging buffers in turn, each
+    uploaded by the kernel) gives each step's plan bit for bit."""
+    g = np.random.default_rng(7)
+    T, S = 1000, 17
+    p = lora.plan(g.integers(0, S, size=T).astype(np.int32), S)
+    for step in range(6):
+        ids = g.integers(0, S, size=T).astype(np.int32)
+        lora.plan_into(p, ids)
+        ref = lora.plan(ids, S, upload=False)
+        torch.cuda.synchronize()
+        got = p.dev.cpu().numpy()
+        nw, ni = p._n_work, ref.info.n_items
+        assert p.info.n_items == ni
+        np.testing.assert_array_equal(got[4 * nw:4 * nw + T], ref.token_order)
+        np.testing.assert_array_equal(got[4 * nw + T:4 * nw + T + S + 1], ref.slot_indptr)
+        np.testing.assert_array_equal(got[:4 * ni].reshape(ni, 4)[:, :3], ref.work[:, :3])

@@ -177,6 +177,18 @@ def test_host_argument_errors():
     assert L.lora_workspace_bytes(None, 10) == 0
 
 
+def test_plan_upload_argument_errors():
+    """lora_plan_upload refuses null pointers and host memory the GPU cannot
+    read (pageable numpy memory; here no GPU at all) before launching
+    anything; zero words is a no-op."""
+    L = lora.lib()
+    buf = np.arange(64, dtype=np.int32)
+    assert L.lora_plan_upload(None, 1, 64, None) == lora.LORA_EINVAL
+    assert L.lora_plan_upload(buf.ctypes.data, None, 64, None) == lora.LORA_EINVAL
+    assert L.lora_plan_upload(None, None, 0, None) == lora.LORA_OK
+    assert L.lora_plan_upload(buf.ctypes.data, 1, 64, None) == lora.LORA_EINVAL
+
+
 def test_multi_host_argument_errors():
     """lora_linear_multi refuses a missing slice array, a slice count outside
     [1, LORA_MAX_SLICES] and a slice without pool before touching the GPU."""
