@@ -187,7 +187,10 @@ __device__ __forceinline__ void shrink_item_slices(const uint16_t* __restrict__ 
                 qok[qb] = q < rs[sl];
                 aq[qb] = ss.A_pool[sl] + ((int64_t)it.slot * r_max + (qok[qb] ? q : 0)) * K;
             }
-            constexpr int U = 4;
+            // 8 rounds of 32 k in flight per wave (shrink_item keeps 4: it
+            // also runs beside the decode GEMM blocks, which more loads in
+            // flight slow down); the k order of every sum is the same
+            constexpr int U = 8;
             for (int s0 = s_beg; s0 < s_end; s0 += U) {
                 u32x4 a[U], b[U][NB];
 #pragma unroll
